@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the Kimi-K3 attention-residual forward (libattnres) on one
+MI355X.
+
+A step is one attnres_fwd call over one batch of synthetic input.  The
+headline workload is the mid prefill: T=1024 tokens, 8 block rows, H=7168,
+delta and output norm on, block_write_idx=3.  The timed region is one replay
+of a hipGraph holding exactly --steps calls, cycling over input sets whose
+total footprint exceeds the 256 MB Infinity Cache, with inputs resident in
+HBM.  `value` is the algorithmic HBM rate (rows read + rows written + weight
+rows, bytes per call) divided by the measured time per call.
+
+Also reported: the single-token decode sweep (T=1, 0/1/4/8 block rows; the
+pages' single-token latency metric) as microseconds per call, cold (rotating
+over ~2400 input sets) and warm (one set), and the fp64 CPU oracle timed on
+the host (the CPU baseline).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --eager --only mid --steps 20   # plain launches, for counters
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from kimi_k3_attention_amd import attnres as A  # noqa: E402
+from kimi_k3_attention_amd import workloads as W  # noqa: E402
+
+METRIC = "AttnRes µs/call (T=1, 0/4/8 blk) + achieved HBM GB/s at T=1024, 8 blk, H=7168"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+DOMINANT_KERNEL = "attnres_row_kernel<8, true, true>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_kernel_mid_prefill.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "kimi_k3_attention_amd", "csrc", f)
+                  for f in ("attnres_kernels.hip", "attnres_internal.h")]
+
+
+def log(*msg):
+    print("[bench]", *msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+class Set:
+    """One resident input set of a workload."""
+
+    def __init__(self, inp: W.Inputs):
+        c = inp.case
+        self.case = c
+        self.prefix = to_dev(inp.prefix)
+        self.delta = to_dev(inp.delta)
+        self.bank = to_dev(inp.bank)
+        self.bank3 = self.bank.as_strided((c.T, c.cap, c.H), (c.token_stride, c.slot_stride, 1))
+        self.res_w = to_dev(inp.res_w)
+        self.rms_w = to_dev(inp.rms_w)
+        self.onw = to_dev(inp.onw)
+        self.out = to_dev(inp.out_init)
+        if self.delta is not None:
+            self.delta.zero_()  # repeated in-place calls stay a fixed point
+
+    def call(self, nb=None, token=None):
+        c = self.case
+        nb = c.nb if nb is None else nb
+        if token is None:
+            A.attnres_fwd(self.prefix, self.delta, self.bank3, nb, self.res_w, self.rms_w, c.eps,
+                          self.onw, c.oeps, c.widx, self.out)
+        else:
+            sl = slice(token, token + 1)
+            A.attnres_fwd(self.prefix[sl], None if self.delta is None else self.delta[sl],
+                          self.bank3[sl], nb, self.res_w, self.rms_w, c.eps, self.onw, c.oeps,
+                          c.widx, self.out[sl])
+
+
+def time_graph(calls, steps: int, replays: int = 1):
+    """Captures `steps` calls (cycling over `calls`) into one hipGraph and
+    returns the elapsed ms of each replay (hipEvents on the launch stream)."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    g.replay()  # one untimed replay: graph upload, first-touch
+    torch.cuda.synchronize()
+    times = []
+    stream = torch.cuda.current_stream()
+    for _ in range(replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del g
+    return times
+
+
+def time_eager(calls, steps: int):
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        calls[i % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def calibration_copy(nbytes: int = 512 << 20, reps: int = 3):
+    """A plain device copy of known size, for scaling the memory-traffic
+    counters (FETCH_SIZE / WRITE_SIZE) of the same profiling run."""
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {reps} x {nbytes} bytes read + written")
+
+
+def bench_mid(steps: int, warmup: int, eager: bool):
+    case = W.mid_prefill()
+    per_call_bytes = case.algorithmic_bytes()
+    footprint = 2 * case.T * case.H * (case.cap + 3)
+    nsets = max(1, -(-2 * MALL_BYTES // footprint))
+    log(f"mid prefill: {nsets} input sets of {footprint / 1e6:.0f} MB, {per_call_bytes} B/call")
+    sets = [Set(W.make_inputs(W.with_(case, seed=case.seed + 100 * r))) for r in range(nsets)]
+    calls = [s.call for s in sets]
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    if eager:
+        ms = time_eager(calls, steps)
+        reps = [ms]
+    else:
+        reps = time_graph(calls, steps, replays=6)
+        ms = reps[0]
+    per_call_ms = ms / steps
+    per_call = [r / steps * 1e3 for r in reps]
+    gbps = per_call_bytes / (per_call_ms * 1e-3) / 1e9
+    log(f"mid prefill: {per_call_ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+    return dict(case=case, sets=sets, per_call_ms=per_call_ms, gbps=gbps, bytes=per_call_bytes,
+                us=dict(p20=pct(per_call, 20), p50=pct(per_call, 50), p80=pct(per_call, 80)),
+                nsets=nsets)
+
+
+def bench_decode(steps: int):
+    """T=1: cold (a different input set per call, ~2400 sets > MALL) and warm
+    (one set), for 0/1/4/8 block rows."""
+    n = 2400
+    case = W.Case("decode_sets", T=n, nb=8, recipe="decode", seed=1)
+    s = Set(W.make_inputs(case))
+    res = {}
+    for nb in (0, 1, 4, 8):
+        cold = [lambda t=t, nb=nb: s.call(nb=nb, token=t) for t in range(n)]
+        warm = [lambda nb=nb: s.call(nb=nb, token=0)]
+        for fn in cold[:50]:
+            fn()
+        k = max(steps, n)
+        tc = time_graph(cold, k, replays=5)
+        tw = time_graph(warm, k, replays=5)
+        res[f"nb{nb}"] = dict(cold_us=pct([t / k * 1e3 for t in tc], 50),
+                              warm_us=pct([t / k * 1e3 for t in tw], 50),
+                              bytes=W.Case("x", T=1, nb=nb).algorithmic_bytes())
+        log(f"decode nb={nb}: cold {res[f'nb{nb}']['cold_us']:.2f} us, warm {res[f'nb{nb}']['warm_us']:.2f} us")
+    return res
+
+
+def cpu_baseline(target_s: float = 10.0):
+    """The fp64 oracle, as it stands, on the host: whole mid-prefill calls
+    (T=1024, 8 block rows) repeated until about target_s of CPU work."""
+    import oracle
+    case = W.mid_prefill()
+    inp = W.make_inputs(case)
+    args = (inp.prefix, inp.delta, inp.bank, case.token_stride, case.slot_stride, case.cap, case.nb,
+            inp.res_w, inp.rms_w, case.eps, inp.onw, case.oeps, case.widx)
+    oracle.attnres_oracle(*args)  # load / build
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        oracle.attnres_oracle(*args)
+        calls += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = (time.perf_counter() - t0) / calls
+    gbps = case.algorithmic_bytes() / dt / 1e9
+    log(f"cpu oracle: {dt * 1e3:.0f} ms/call, {gbps:.3f} GB/s")
+    return dict(value=round(gbps, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{calls} whole calls of the T=1024 nb=8 workload (single-threaded C, fp64), "
+                       f"{dt * 1e3:.0f} ms/call")
+
+
+def load_traffic(per_call_ms):
+    """HBM bytes per launch from the committed counter runs, if they were taken
+    on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--eager", action="store_true", help="plain launches instead of a hipGraph")
+    ap.add_argument("--only", choices=["mid", "decode"], default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--calibrate", action="store_true", help="run the known-size copy for counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the attention-residual op shards by tokens with no exchange, so the "
+              "single-GPU figure is the per-GPU rate", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+    A.attnres_init()
+    if args.calibrate:
+        calibration_copy()
+
+    mid = None if args.only == "decode" else bench_mid(args.steps, args.warmup, args.eager)
+    decode = None if (args.only == "mid" or args.eager) else bench_decode(args.steps)
+    if A.attnres_device_status() != A.ATTNRES_OK:
+        raise SystemExit("device wait flag raised during the benchmark")
+    cpu = None if (args.no_cpu or args.only) else cpu_baseline()
+
+    line = {"metric": METRIC}
+    if mid is not None:
+        achieved = mid["gbps"]
+        line.update({
+            "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(mid["per_call_ms"], 6),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "storage_dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "mid prefill: T=1024 tokens, 8 block rows, H=7168, delta and "
+                                   "output norm on, block_write_idx=3, bf16, dense bank",
+                       "T": 1024, "num_blocks": 8, "H": 7168, "input_sets": mid["nsets"],
+                       "timing": "eager" if args.eager else "hipGraph replay",
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "hbm", "kernel": DOMINANT_KERNEL, "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic(mid["per_call_ms"]),
+                         "algorithmic_bytes_per_launch": mid["bytes"]},
+            "mid_prefill_us_per_call": {k: round(v, 3) for k, v in mid["us"].items()},
+        })
+    if decode is not None:
+        line["decode_T1_us_per_call"] = {k: round(v["cold_us"], 3) for k, v in decode.items()}
+        line["decode_T1_warm_us_per_call"] = {k: round(v["warm_us"], 3) for k, v in decode.items()}
+        if mid is None:
+            line.update({"value": round(decode["nb8"]["cold_us"], 3), "unit": "us/call",
+                         "higher_is_better": False})
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    line["kernel_source_hash"] = kernel_source_hash()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * attnres.h -- C ABI of libattnres: the Kimi-K3 attention-residual (AttnRes)
+ * forward on AMD MI355X (gfx950).
+ *
+ * The operation (defined by the vllm-ascend PR #14840 page, author's
+ * "Implementation walkthrough", and the prhub digest of vLLM PR #54261,
+ * "Implementation breakdown" items 1-3 and the kernel snippet under "Key
+ * source snippets"):
+ *
+ *   for every token t:
+ *     cur      = delta ? bf16_RNE(prefix[t] + delta[t]) : prefix[t]
+ *     sources  = blocks[t, 0], ..., blocks[t, num_blocks-1], cur
+ *     q        = rms_w * res_w                      (fused query, PR #50185)
+ *     logit_j  = sum_h q[h] * x_j[h] / sqrt(mean_h(x_j^2) + rms_eps)
+ *     p        = softmax(logit)                     (over the num_blocks+1 sources)
+ *     y        = sum_j p_j * x_j                    (raw rows)
+ *     out[t]   = bf16_RNE(output_norm_weight
+ *                  ? y / sqrt(mean_h(y^2) + output_norm_eps) * output_norm_weight
+ *                  : y)
+ *     if delta:               prefix[t] = cur                     (in place)
+ *     if block_write_idx>=0:  blocks[t, block_write_idx] = cur    (in place)
+ *
+ * All reads see the state before the call (a written slot that is also a
+ * source contributes its old value).  Bank slots num_blocks..max_blocks-1 are
+ * never read, and nothing but out, prefix (with a delta) and the one bank row
+ * per token is ever written.
+ *
+ * Tensors are bf16 (passed as raw 16-bit patterns) in device memory.  The
+ * library keeps no pointer after a call returns; the caller owns every buffer
+ * and keeps it alive until the stream work completes.  Arithmetic is fp32.
+ *
+ * Errors: every entry point returns ATTNRES_OK (0) or a negative code.  All
+ * argument checks run on the host before any GPU work, so a rejected call
+ * launches nothing and touches no buffer.
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define ATTNRES_OK 0
+#define ATTNRES_E_NULL -1        /* a required pointer is NULL */
+#define ATTNRES_E_SHAPE -2       /* T < 0, H <= 0, max_blocks < 0, or sizes too large */
+#define ATTNRES_E_UNSUPPORTED -3 /* H != 7168, or a forced path that cannot run these sizes */
+#define ATTNRES_E_NUM_BLOCKS -4  /* num_blocks < 0, > 8 or > max_blocks */
+#define ATTNRES_E_WRITE_IDX -5   /* block_write_idx < -1 or >= max_blocks */
+#define ATTNRES_E_ALIGN -6       /* a pointer not 16-byte aligned, or a bank stride not a multiple of 8 */
+#define ATTNRES_E_STRIDE -7      /* negative bank strides, or bank rows that overlap */
+#define ATTNRES_E_ALIAS -8       /* a written buffer overlaps another argument */
+#define ATTNRES_E_EPS -9         /* an epsilon that is negative or not finite */
+#define ATTNRES_E_NOT_INIT -10   /* the split path needs attnres_init() first (stream is capturing) */
+#define ATTNRES_E_HIP -11        /* a HIP call failed; see attnres_last_hip_error() */
+#define ATTNRES_E_PATH -12       /* unknown path selector */
+#define ATTNRES_E_DEVICE_WAIT -13 /* a split-path cross-workgroup wait gave up (device flag) */
+
+/* ---- path selectors for attnres_fwd_path -------------------------------- */
+#define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: split for few tokens, row otherwise */
+#define ATTNRES_PATH_ROW 1   /* one workgroup per token */
+#define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (T <= 256) */
+
+/* Largest T the split path accepts (its per-device workspace). */
+#define ATTNRES_SPLIT_MAX_TOKENS 256
+
+/*
+ * attnres_fwd -- the forward above, enqueued on `stream`.
+ *
+ *   prefix   [T, H] bf16, row stride H, device.  Read; overwritten with cur
+ *            when delta != NULL.
+ *   delta    [T, H] bf16, row stride H, device, or NULL (no delta).
+ *   blocks   the block bank: element (t, i, h) at
+ *            blocks[t*block_token_stride + i*block_slot_stride + h], for
+ *            i < max_blocks.  Strides in elements, >= 0, multiples of 8, rows
+ *            must not overlap.  May be NULL only when num_blocks == 0 and
+ *            block_write_idx == -1.  Slots 0..num_blocks-1 are the sources;
+ *            slot block_write_idx (if >= 0) receives cur.
+ *   max_blocks   bank capacity (slots per token); num_blocks <= max_blocks.
+ *   num_blocks   valid slots, 0..8.
+ *   res_w, rms_w [H] bf16, device: scoring projection and RMSNorm weight.
+ *   rms_eps      >= 0, finite.
+ *   output_norm_weight [H] bf16, device, or NULL = no output norm.
+ *   output_norm_eps    >= 0, finite (ignored without an output norm).
+ *   block_write_idx    -1 = no bank write, else 0..max_blocks-1.
+ *   out      [T, H] bf16, row stride H, device; must not overlap any input.
+ *   T, H     tokens (>= 0; T == 0 is a no-op) and hidden size (7168).
+ *   stream   a hipStream_t (NULL = the default stream).
+ *
+ * All device pointers must be 16-byte aligned.  Asynchronous: returns after
+ * enqueueing.  No allocation or host synchronisation happens once the split
+ * path's workspace exists (attnres_init, or the first uncaptured call that
+ * needs it), so calls can be captured into a hipGraph.  Calls that use the
+ * split path share one workspace per device and must be ordered on one stream.
+ */
+int attnres_fwd(void *prefix, const void *delta, void *blocks,
+                int64_t block_token_stride, int64_t block_slot_stride,
+                int max_blocks, int num_blocks,
+                const void *res_w, const void *rms_w, float rms_eps,
+                const void *output_norm_weight, float output_norm_eps,
+                int block_write_idx, void *out, int64_t T, int64_t H,
+                void *stream);
+
+/* attnres_fwd with an explicit path (ATTNRES_PATH_*); both paths compute the
+ * same result within the fp32 rounding of their reduction orders. */
+int attnres_fwd_path(void *prefix, const void *delta, void *blocks,
+                     int64_t block_token_stride, int64_t block_slot_stride,
+                     int max_blocks, int num_blocks,
+                     const void *res_w, const void *rms_w, float rms_eps,
+                     const void *output_norm_weight, float output_norm_eps,
+                     int block_write_idx, void *out, int64_t T, int64_t H,
+                     void *stream, int path);
+
+/* The host-side argument checks of attnres_fwd, alone.  Makes no HIP call and
+ * dereferences no pointer, so it runs without a GPU. */
+int attnres_validate(const void *prefix, const void *delta, const void *blocks,
+                     int64_t block_token_stride, int64_t block_slot_stride,
+                     int max_blocks, int num_blocks,
+                     const void *res_w, const void *rms_w, float rms_eps,
+                     const void *output_norm_weight, float output_norm_eps,
+                     int block_write_idx, const void *out, int64_t T, int64_t H);
+
+/* Allocates and clears the split path's workspace on `device` (a few hundred
+ * KB: cross-workgroup counters, partial sums and a fault flag).  Idempotent.
+ * Call it outside stream capture. */
+int attnres_init(int device);
+
+/* Frees every device's workspace.  No call may be in flight. */
+void attnres_shutdown(void);
+
+/* Reads (synchronously) and clears the split path's device fault flag on
+ * `device`: ATTNRES_E_DEVICE_WAIT if a cross-workgroup wait ever gave up since
+ * the last check (the counters are then reset), else ATTNRES_OK. */
+int attnres_device_status(int device);
+
+/* Static description of a status code. */
+const char *attnres_strerror(int status);
+
+/* The hipError_t of the last failed HIP call in this library (0 if none). */
+int attnres_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNRES_H */

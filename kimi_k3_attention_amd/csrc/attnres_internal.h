@@ -1,0 +1,38 @@
+// Internal declarations shared by the host-side translation units of
+// libattnres (validation and launch).  Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+
+#include "../../include/attnres.h"
+
+namespace attnres {
+
+constexpr int kHidden = 7168;          // the only hidden size the kernels are built for
+constexpr int kMaxBlocks = 8;          // bank rows a token may mix
+constexpr int64_t kMaxTokens = 2147483647LL;   // grid.x limit of the row path
+constexpr int64_t kMaxStride = int64_t(1) << 46;
+
+struct FwdArgs {
+  const void *prefix = nullptr;
+  const void *delta = nullptr;
+  const void *blocks = nullptr;
+  int64_t block_token_stride = 0;
+  int64_t block_slot_stride = 0;
+  int max_blocks = 0;
+  int num_blocks = 0;
+  const void *res_w = nullptr;
+  const void *rms_w = nullptr;
+  float rms_eps = 0.f;
+  const void *output_norm_weight = nullptr;
+  float output_norm_eps = 0.f;
+  int block_write_idx = -1;
+  const void *out = nullptr;
+  int64_t T = 0;
+  int64_t H = 0;
+};
+
+int validate(const FwdArgs &a);
+const char *strerror_text(int status);
+
+}  // namespace attnres

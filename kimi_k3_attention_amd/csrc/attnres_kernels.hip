@@ -1,0 +1,669 @@
+// libattnres kernels and launch layer: the Kimi-K3 attention-residual forward
+// on MI355X (gfx950, CDNA4, wave64).
+//
+// The operation is defined in include/attnres.h (vllm-ascend PR #14840,
+// "Implementation walkthrough"; prhub digest of vLLM PR #54261, kernel
+// snippet under "Key source snippets").  The work is a streaming reduction:
+// per token it reads num_blocks + 1 (+1 with a delta) rows of 7168 bf16 once,
+// reduces each row to two scalars, and writes 1-3 rows.  Arithmetic intensity
+// is about 2 flop/byte, far below the fp32 ridge, so HBM bandwidth bounds it
+// and no matrix core is involved.
+//
+// Layout of the work: a "segment" is 8 consecutive bf16 (16 bytes); a row is
+// 896 segments.  A lane owns one segment of every source row of its token, so
+// each row is read with one 128-bit load per lane and the whole token stays in
+// VGPRs between the reduction and the mixture (no second read of any row).
+//
+//  * Row path (many tokens): one 896-lane workgroup (14 waves) per token.
+//    Per-lane fp32 sum-of-squares and query dot for every source, a wave64
+//    DPP reduction, a cross-wave reduction through LDS, logits, the softmax
+//    normaliser in online form, the fp32 mixture, the optional output RMSNorm
+//    (a second LDS reduction), bf16 round-to-nearest-even stores.
+//  * Split path (few tokens): 14 single-wave workgroups per token, each owning
+//    512 elements of every row, so a single token is spread over 14 CUs.
+//    Partial sums are exchanged through a small device workspace with
+//    agent-scope release/acquire atomics (the 8 XCDs do not share L2) and a
+//    monotonic per-token arrival counter, so no reset is needed between calls
+//    or graph replays.  Waits are bounded: a wait that gives up raises a
+//    device flag instead of hanging.
+//
+// Compile-time specialisation on num_blocks (0..8), delta and output norm;
+// block_write_idx stays a uniform runtime branch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <mutex>
+
+#include "attnres_internal.h"
+
+namespace attnres {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kSeg = 8;                       // bf16 per 16-byte segment
+constexpr int kSegs = kHidden / kSeg;         // 896 segments per row
+constexpr int kWave = 64;
+constexpr int kRowThreads = kSegs;            // row path: one segment per lane
+constexpr int kRowWaves = kRowThreads / kWave;  // 14
+constexpr int kParts = 14;                    // split path: workgroups per token
+constexpr int kPartThreads = kSegs / kParts;  // 64 = one wave
+constexpr int kSlot = 20;                     // floats per (token, part) workspace slot
+constexpr int kSlotYsq = kSlot - 1;           // where a part's sum of y^2 goes
+constexpr int kCounterStride = 16;            // uint64 words between token counters (128 B)
+constexpr int kSpinLimit = 1 << 20;           // bounded cross-workgroup wait
+constexpr int kAutoSplitMaxTokens = 32;       // attnres_fwd uses the split path up to here
+constexpr float kInvHidden = 1.0f / kHidden;
+
+static_assert(kSegs * kSeg == kHidden, "hidden size must be a multiple of 8");
+static_assert(kRowThreads % kWave == 0, "row workgroup must be whole waves");
+static_assert(kPartThreads == kWave, "a split part is one wave");
+static_assert(2 * (kMaxBlocks + 1) < kSlotYsq, "workspace slot too small");
+
+struct KParams {
+  uint16_t *prefix;
+  const uint16_t *delta;
+  uint16_t *blocks;
+  const uint16_t *res_w;
+  const uint16_t *rms_w;
+  const uint16_t *onw;
+  uint16_t *out;
+  int64_t tok_stride;
+  int64_t slot_stride;
+  float rms_eps;
+  float out_eps;
+  int widx;
+  int T;
+  float *ws_part;
+  unsigned long long *ws_count;
+  unsigned *ws_flag;
+};
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+// Streaming rows are touched exactly once: non-temporal 128-bit accesses keep
+// them from evicting the weights, which every workgroup re-reads from L2.
+__device__ __forceinline__ u32x4 load_stream(const uint16_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x4 load_cached(const uint16_t *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void store_stream(uint16_t *p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16x2, round to nearest even (gfx950 converts in one
+// instruction under the default rounding mode).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_src(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave; the total is valid in lane 63.  Butterfly
+// inside each 16-lane row (xor 1, xor 2, half-row mirror, row mirror: every
+// lane of a row then holds the row sum), then row 0 is folded into row 1 and
+// row 2 into row 3 (broadcast of lane 15 / 47), then rows 0+1 into row 3
+// (broadcast of lane 31).  The order is fixed, so results are repeatable.
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  v += dpp_src<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_src<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_src<0x141>(v);       // row_half_mirror
+  v += dpp_src<0x140>(v);       // row_mirror
+  v += dpp_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_src<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Hides the packed rows from the optimiser between the reduction and the
+// mixture, so it keeps 4 packed words per row live instead of 8 unpacked
+// fp32 values (the unpack is one shift or mask per element, cheaper than the
+// occupancy the extra registers would cost).  Emits no instruction.
+template <int NS>
+__device__ __forceinline__ void keep_packed(u32x4 (&x)[NS]) {
+#pragma unroll
+  for (int j = 0; j < NS; ++j) asm volatile("" : "+v"(x[j]));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Everything one lane reads, issued in one burst: the L2-resident weights
+// first (the wait counter is in order, so the query can be formed while the
+// rows are still in flight), then the bank rows, prefix and delta.  Row bases
+// are workgroup-uniform (scalar registers); the lane adds its 16-byte segment
+// offset.
+template <int NB, bool DELTA, bool ONORM>
+struct TokenLoads {
+  u32x4 rms, res, onw;  // weights
+  u32x4 x[NB + 1];      // bank slots 0..NB-1, then prefix (cur after finish_cur)
+  u32x4 d;              // delta
+
+  __device__ __forceinline__ void issue(const KParams &p, int64_t t, int seg) {
+    const int off = seg * kSeg;
+    rms = load_cached(p.rms_w + off);
+    res = load_cached(p.res_w + off);
+    if constexpr (ONORM) onw = load_cached(p.onw + off);
+    const uint16_t *bank = p.blocks + t * p.tok_stride;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) x[j] = load_stream(bank + j * p.slot_stride + off);
+    x[NB] = load_stream(p.prefix + t * kHidden + off);
+    if constexpr (DELTA) d = load_stream(p.delta + t * kHidden + off);
+    // Keep the scheduler from sinking any of these loads below the arithmetic.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Fused query q = rms_w * res_w for this lane's 8 elements (exact in fp32).
+  __device__ __forceinline__ void query(float (&q)[8]) const {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      q[2 * k] = bf_lo(rms[k]) * bf_lo(res[k]);
+      q[2 * k + 1] = bf_hi(rms[k]) * bf_hi(res[k]);
+    }
+  }
+
+  // cur = bf16_RNE(prefix + delta) into x[NB].  The fp32 sum of two bf16
+  // values is within 2^-24 (relative) of the exact sum, which is never close
+  // enough to a bf16 rounding boundary to change the rounded result.
+  __device__ __forceinline__ void finish_cur() {
+    if constexpr (DELTA) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        x[NB][k] = pack_bf16x2(bf_lo(x[NB][k]) + bf_lo(d[k]), bf_hi(x[NB][k]) + bf_hi(d[k]));
+    }
+  }
+};
+
+// Per-lane partial sum of squares and query dot of one source row segment.
+__device__ __forceinline__ void row_partials(const u32x4 &x, const float (&q)[8], float &ss,
+                                             float &dq) {
+  float s = 0.f, d = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = bf_lo(x[k]), b = bf_hi(x[k]);
+    s = fmaf(a, a, s);
+    s = fmaf(b, b, s);
+    d = fmaf(q[2 * k], a, d);
+    d = fmaf(q[2 * k + 1], b, d);
+  }
+  ss = s;
+  dq = d;
+}
+
+// Softmax weights of the NS sources.  Lane j (< NS) holds logit j.  The
+// normaliser is accumulated in online form (running max m, running sum z of
+// exp(l - m), rescaled whenever the max moves); every lane computes the same
+// uniform values.
+template <int NS>
+__device__ __forceinline__ void softmax_weights(float logit_lane, float (&pw)[NS]) {
+  float l[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) l[j] = lane_value(logit_lane, j);
+  float m = l[0], z = 1.f;
+#pragma unroll
+  for (int j = 1; j < NS; ++j) {
+    const float mn = fmaxf(m, l[j]);
+    z = z * __expf(m - mn) + __expf(l[j] - mn);
+    m = mn;
+  }
+  const float inv = 1.f / z;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) pw[j] = __expf(l[j] - m) * inv;
+}
+
+// y = sum_j p_j x_j over the raw rows, fp32.
+template <int NS>
+__device__ __forceinline__ void mix(const u32x4 (&x)[NS], const float (&pw)[NS], float (&y)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = 0.f;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      y[2 * k] = fmaf(pw[j], bf_lo(x[j][k]), y[2 * k]);
+      y[2 * k + 1] = fmaf(pw[j], bf_hi(x[j][k]), y[2 * k + 1]);
+    }
+  }
+}
+
+__device__ __forceinline__ float sum_sq8(const float (&y)[8]) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s = fmaf(y[k], y[k], s);
+  return s;
+}
+
+template <bool ONORM>
+__device__ __forceinline__ void store_token(const KParams &p, int64_t t, int seg, const float (&y)[8],
+                                            float rsig, const u32x4 &w) {
+  const int64_t h0 = int64_t(seg) * kSeg;
+  u32x4 o;
+  if constexpr (ONORM) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = pack_bf16x2(y[2 * k] * rsig * bf_lo(w[k]), y[2 * k + 1] * rsig * bf_hi(w[k]));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
+  }
+  store_stream(p.out + t * kHidden + h0, o);
+}
+
+// In-place writes of cur, after every read of this lane's elements.
+template <bool DELTA>
+__device__ __forceinline__ void store_cur(const KParams &p, int64_t t, int seg, const u32x4 &cur) {
+  const int64_t h0 = int64_t(seg) * kSeg;
+  if constexpr (DELTA) store_stream(p.prefix + t * kHidden + h0, cur);
+  if (p.widx >= 0) store_stream(p.blocks + t * p.tok_stride + p.widx * p.slot_stride + h0, cur);
+}
+
+// ---------------------------------------------------------------------------
+// row path: one workgroup per token
+// ---------------------------------------------------------------------------
+
+template <int NB, bool DELTA, bool ONORM>
+__global__ void __launch_bounds__(kRowThreads) attnres_row_kernel(KParams p) {
+  constexpr int NS = NB + 1;
+  __shared__ float s_red[kRowWaves][2 * NS];
+  __shared__ float s_ysq[kRowWaves];
+
+  const int64_t t = blockIdx.x;
+  const int seg = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+
+  TokenLoads<NB, DELTA, ONORM> in;
+  in.issue(p, t, seg);
+  float q[8];
+  in.query(q);
+  in.finish_cur();
+  u32x4 (&x)[NS] = in.x;
+
+  // Each source is reduced and published as soon as its partials exist, so
+  // only two partial sums are live at a time.
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    float s, d;
+    row_partials(x[j], q, s, d);
+    s = wave_sum_lane63(s);
+    d = wave_sum_lane63(d);
+    if (lane == kWave - 1) {
+      s_red[wave][j] = s;
+      s_red[wave][NS + j] = d;
+    }
+  }
+  keep_packed<NS>(x);
+  __syncthreads();
+
+  float logit = 0.f;
+  if (lane < NS) {
+    float s = 0.f, d = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      s += s_red[w][lane];
+      d += s_red[w][NS + lane];
+    }
+    logit = d * rsqrtf(s * kInvHidden + p.rms_eps);
+  }
+  float pw[NS];
+  softmax_weights<NS>(logit, pw);
+  float y[8];
+  mix<NS>(x, pw, y);
+
+  float rsig = 1.f;
+  if constexpr (ONORM) {
+    const float sy = wave_sum_lane63(sum_sq8(y));
+    if (lane == kWave - 1) s_ysq[wave] = sy;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) tot += s_ysq[w];
+    rsig = rsqrtf(tot * kInvHidden + p.out_eps);
+  }
+  store_token<ONORM>(p, t, seg, y, rsig, in.onw);
+  store_cur<DELTA>(p, t, seg, x[NB]);
+}
+
+// ---------------------------------------------------------------------------
+// split path: kParts single-wave workgroups per token
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float load_agent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrive at the token's counter and wait until all kParts workgroups of this
+// phase have arrived.  The counter only grows: the k-th phase of a token
+// completes when it reaches k * kParts, so arrival value `old` belongs to the
+// phase ending at (old / kParts + 1) * kParts.  Called by one lane.
+__device__ __forceinline__ void arrive_and_wait(unsigned long long *cnt, unsigned *flag) {
+  const unsigned long long old =
+      __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long target = (old / kParts + 1) * kParts;
+  int spins = 0;
+  while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+template <int NB, bool DELTA, bool ONORM>
+__global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) {
+  constexpr int NS = NB + 1;
+  const int64_t t = blockIdx.x / kParts;
+  const int part = blockIdx.x - int(t) * kParts;
+  const int lane = threadIdx.x;
+  const int seg = part * kPartThreads + lane;
+
+  TokenLoads<NB, DELTA, ONORM> in;
+  in.issue(p, t, seg);
+  float q[8];
+  in.query(q);
+  in.finish_cur();
+  u32x4 (&x)[NS] = in.x;
+
+  float *const tok_ws = p.ws_part + size_t(t) * kParts * kSlot;
+  unsigned long long *const cnt = p.ws_count + size_t(t) * kCounterStride;
+  float *const slot = tok_ws + part * kSlot;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    float s, d;
+    row_partials(x[j], q, s, d);
+    s = wave_sum_lane63(s);
+    d = wave_sum_lane63(d);
+    if (lane == kWave - 1) {
+      slot[j] = s;
+      slot[NS + j] = d;
+    }
+  }
+  keep_packed<NS>(x);
+  if (lane == kWave - 1) arrive_and_wait(cnt, p.ws_flag);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  float logit = 0.f;
+  if (lane < NS) {
+    float s = 0.f, d = 0.f;
+#pragma unroll
+    for (int r = 0; r < kParts; ++r) {
+      s += load_agent(tok_ws + r * kSlot + lane);
+      d += load_agent(tok_ws + r * kSlot + NS + lane);
+    }
+    logit = d * rsqrtf(s * kInvHidden + p.rms_eps);
+  }
+  float pw[NS];
+  softmax_weights<NS>(logit, pw);
+  float y[8];
+  mix<NS>(x, pw, y);
+
+  float rsig = 1.f;
+  if constexpr (ONORM) {
+    const float sy = wave_sum_lane63(sum_sq8(y));
+    if (lane == kWave - 1) {
+      tok_ws[part * kSlot + kSlotYsq] = sy;
+      arrive_and_wait(cnt, p.ws_flag);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    float tot = 0.f;
+#pragma unroll
+    for (int r = 0; r < kParts; ++r) tot += load_agent(tok_ws + r * kSlot + kSlotYsq);
+    rsig = rsqrtf(tot * kInvHidden + p.out_eps);
+  }
+  store_token<ONORM>(p, t, seg, y, rsig, in.onw);
+  store_cur<DELTA>(p, t, seg, x[NB]);
+}
+
+// ---------------------------------------------------------------------------
+// specialisation tables
+// ---------------------------------------------------------------------------
+
+using KernelFn = void (*)(KParams);
+
+template <int NB>
+KernelFn row_fn(bool d, bool o) {
+  if (d) return o ? attnres_row_kernel<NB, true, true> : attnres_row_kernel<NB, true, false>;
+  return o ? attnres_row_kernel<NB, false, true> : attnres_row_kernel<NB, false, false>;
+}
+template <int NB>
+KernelFn split_fn(bool d, bool o) {
+  if (d) return o ? attnres_split_kernel<NB, true, true> : attnres_split_kernel<NB, true, false>;
+  return o ? attnres_split_kernel<NB, false, true> : attnres_split_kernel<NB, false, false>;
+}
+
+KernelFn pick(bool split, int nb, bool d, bool o) {
+  switch (nb) {
+#define ATTNRES_CASE(N) \
+  case N: return split ? split_fn<N>(d, o) : row_fn<N>(d, o);
+    ATTNRES_CASE(0) ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
+    ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
+#undef ATTNRES_CASE
+    default: return nullptr;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-device split-path workspace
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+constexpr size_t kPartBytes = size_t(ATTNRES_SPLIT_MAX_TOKENS) * kParts * kSlot * sizeof(float);
+constexpr size_t kCountBytes = size_t(ATTNRES_SPLIT_MAX_TOKENS) * kCounterStride * 8;
+constexpr size_t kFlagBytes = 256;
+constexpr size_t kWorkspaceBytes = kPartBytes + kCountBytes + kFlagBytes;
+
+struct DeviceWorkspace {
+  void *base = nullptr;
+  float *part = nullptr;
+  unsigned long long *count = nullptr;
+  unsigned *flag = nullptr;
+};
+
+DeviceWorkspace g_ws[kMaxDevices];
+std::mutex g_ws_mu;
+std::atomic<int> g_last_hip{0};
+
+int hip_fail(hipError_t e) {
+  g_last_hip.store(int(e));
+  return ATTNRES_E_HIP;
+}
+
+int init_device_locked(int device) {
+  if (g_ws[device].base) return ATTNRES_OK;
+  int prev = 0;
+  hipError_t e = hipGetDevice(&prev);
+  if (e != hipSuccess) return hip_fail(e);
+  if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e);
+  void *base = nullptr;
+  e = hipMalloc(&base, kWorkspaceBytes);
+  if (e == hipSuccess) e = hipMemset(base, 0, kWorkspaceBytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    if (base) (void)hipFree(base);
+    (void)hipSetDevice(prev);
+    return hip_fail(e);
+  }
+  DeviceWorkspace &w = g_ws[device];
+  w.base = base;
+  w.part = static_cast<float *>(base);
+  w.count = reinterpret_cast<unsigned long long *>(static_cast<char *>(base) + kPartBytes);
+  w.flag = reinterpret_cast<unsigned *>(static_cast<char *>(base) + kPartBytes + kCountBytes);
+  (void)hipSetDevice(prev);
+  return ATTNRES_OK;
+}
+
+int fwd_impl(const FwdArgs &a, void *stream, int path) {
+  if (path != ATTNRES_PATH_AUTO && path != ATTNRES_PATH_ROW && path != ATTNRES_PATH_SPLIT)
+    return ATTNRES_E_PATH;
+  int rc = validate(a);
+  if (rc != ATTNRES_OK) return rc;
+  if (a.T == 0) return ATTNRES_OK;
+
+  bool split = path == ATTNRES_PATH_SPLIT ||
+               (path == ATTNRES_PATH_AUTO && a.T <= kAutoSplitMaxTokens);
+  if (split && a.T > ATTNRES_SPLIT_MAX_TOKENS) return ATTNRES_E_UNSUPPORTED;
+
+  KParams kp{};
+  kp.prefix = static_cast<uint16_t *>(const_cast<void *>(a.prefix));
+  kp.delta = static_cast<const uint16_t *>(a.delta);
+  kp.blocks = static_cast<uint16_t *>(const_cast<void *>(a.blocks));
+  kp.res_w = static_cast<const uint16_t *>(a.res_w);
+  kp.rms_w = static_cast<const uint16_t *>(a.rms_w);
+  kp.onw = static_cast<const uint16_t *>(a.output_norm_weight);
+  kp.out = static_cast<uint16_t *>(const_cast<void *>(a.out));
+  kp.tok_stride = a.block_token_stride;
+  kp.slot_stride = a.block_slot_stride;
+  kp.rms_eps = a.rms_eps;
+  kp.out_eps = a.output_norm_weight ? a.output_norm_eps : 0.f;
+  kp.widx = a.block_write_idx;
+  kp.T = int(a.T);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (split) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    if (!g_ws[dev].base) {
+      hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+      e = hipStreamIsCapturing(s, &st);
+      if (e != hipSuccess) return hip_fail(e);
+      if (st != hipStreamCaptureStatusNone) return ATTNRES_E_NOT_INIT;
+      rc = init_device_locked(dev);
+      if (rc != ATTNRES_OK) return rc;
+    }
+    kp.ws_part = g_ws[dev].part;
+    kp.ws_count = g_ws[dev].count;
+    kp.ws_flag = g_ws[dev].flag;
+  }
+
+  KernelFn fn = pick(split, a.num_blocks, a.delta != nullptr, a.output_norm_weight != nullptr);
+  if (!fn) return ATTNRES_E_NUM_BLOCKS;
+  const dim3 grid = split ? dim3(unsigned(a.T) * kParts) : dim3(unsigned(a.T));
+  const dim3 block = split ? dim3(kPartThreads) : dim3(kRowThreads);
+  void *args[] = {&kp};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, args, 0, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return ATTNRES_OK;
+}
+
+FwdArgs make_args(const void *prefix, const void *delta, const void *blocks, int64_t ts,
+                  int64_t ss, int max_blocks, int num_blocks, const void *res_w,
+                  const void *rms_w, float rms_eps, const void *onw, float oeps, int widx,
+                  const void *out, int64_t T, int64_t H) {
+  FwdArgs a;
+  a.prefix = prefix;
+  a.delta = delta;
+  a.blocks = blocks;
+  a.block_token_stride = ts;
+  a.block_slot_stride = ss;
+  a.max_blocks = max_blocks;
+  a.num_blocks = num_blocks;
+  a.res_w = res_w;
+  a.rms_w = rms_w;
+  a.rms_eps = rms_eps;
+  a.output_norm_weight = onw;
+  a.output_norm_eps = oeps;
+  a.block_write_idx = widx;
+  a.out = out;
+  a.T = T;
+  a.H = H;
+  return a;
+}
+
+}  // namespace
+}  // namespace attnres
+
+using namespace attnres;
+
+extern "C" int attnres_fwd(void *prefix, const void *delta, void *blocks,
+                           int64_t block_token_stride, int64_t block_slot_stride, int max_blocks,
+                           int num_blocks, const void *res_w, const void *rms_w, float rms_eps,
+                           const void *output_norm_weight, float output_norm_eps,
+                           int block_write_idx, void *out, int64_t T, int64_t H, void *stream) {
+  return fwd_impl(make_args(prefix, delta, blocks, block_token_stride, block_slot_stride,
+                            max_blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
+                            output_norm_eps, block_write_idx, out, T, H),
+                  stream, ATTNRES_PATH_AUTO);
+}
+
+extern "C" int attnres_fwd_path(void *prefix, const void *delta, void *blocks,
+                                int64_t block_token_stride, int64_t block_slot_stride,
+                                int max_blocks, int num_blocks, const void *res_w,
+                                const void *rms_w, float rms_eps, const void *output_norm_weight,
+                                float output_norm_eps, int block_write_idx, void *out, int64_t T,
+                                int64_t H, void *stream, int path) {
+  return fwd_impl(make_args(prefix, delta, blocks, block_token_stride, block_slot_stride,
+                            max_blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
+                            output_norm_eps, block_write_idx, out, T, H),
+                  stream, path);
+}
+
+extern "C" int attnres_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return hip_fail(e);
+  if (device >= n) return ATTNRES_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  return init_device_locked(device);
+}
+
+extern "C" void attnres_shutdown(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  for (int d = 0; d < kMaxDevices; ++d) {
+    if (g_ws[d].base) {
+      int prev = 0;
+      (void)hipGetDevice(&prev);
+      (void)hipSetDevice(d);
+      (void)hipDeviceSynchronize();
+      (void)hipFree(g_ws[d].base);
+      (void)hipSetDevice(prev);
+      g_ws[d] = DeviceWorkspace{};
+    }
+  }
+}
+
+extern "C" int attnres_device_status(int device) {
+  if (device < 0 || device >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  DeviceWorkspace &w = g_ws[device];
+  if (!w.base) return ATTNRES_OK;
+  int prev = 0;
+  hipError_t e = hipGetDevice(&prev);
+  if (e != hipSuccess) return hip_fail(e);
+  if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e);
+  unsigned flag = 0;
+  e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(&flag, w.flag, sizeof flag, hipMemcpyDeviceToHost);
+  int rc = ATTNRES_OK;
+  if (e == hipSuccess && flag != 0) {
+    // A wait gave up: phases may be out of step, so restart every counter.
+    e = hipMemset(w.base, 0, kWorkspaceBytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    rc = ATTNRES_E_DEVICE_WAIT;
+  }
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) return hip_fail(e);
+  return rc;
+}
+
+extern "C" int attnres_last_hip_error(void) { return g_last_hip.load(); }

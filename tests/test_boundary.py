@@ -1,0 +1,159 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every entry point
+include/attnres.h declares, and its host-side checks reject every invalid
+argument with the documented code before any GPU work (no GPU needed: these
+calls never dereference a pointer)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+H = 7168
+MB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attnres_[a-z_]+)\s*\(", text)))
+
+
+def _declared_constants():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2))
+            for m in re.finditer(r"#define\s+(ATTNRES_[A-Z_]+)\s+(-?\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def A():
+    from kimi_k3_attention_amd import attnres
+    return attnres
+
+
+def test_library_exports_every_declared_symbol(A):
+    names = _declared_functions()
+    assert {"attnres_fwd", "attnres_fwd_path", "attnres_validate", "attnres_init",
+            "attnres_shutdown", "attnres_strerror"} <= set(names)
+    lib = A.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"symbols declared but not exported: {missing}"
+
+
+def test_binding_status_table_matches_header(A):
+    consts = _declared_constants()
+    for name, code in consts.items():
+        if name.startswith("ATTNRES_E_") or name == "ATTNRES_OK":
+            assert A.STATUS[code] == name
+            assert A.attnres_strerror(code) != "unknown status"
+    assert consts["ATTNRES_SPLIT_MAX_TOKENS"] == A.ATTNRES_SPLIT_MAX_TOKENS
+    assert consts["ATTNRES_PATH_ROW"] == A.ATTNRES_PATH_ROW
+    assert consts["ATTNRES_PATH_SPLIT"] == A.ATTNRES_PATH_SPLIT
+
+
+def _args(**kw):
+    """A valid argument set with fake, 16-byte aligned, disjoint addresses."""
+    T = kw.pop("T", 4)
+    a = dict(prefix=0x10000000, delta=0x20000000, blocks=0x40000000, ts=8 * H, ss=H, cap=8, nb=4,
+             res_w=0x30000000, rms_w=0x30100000, eps=1e-6, onw=0x30200000, oeps=1e-6, widx=-1,
+             out=0x50000000, T=T, H=H)
+    a.update(kw)
+    return a
+
+
+def _validate(A, a):
+    return A.lib().attnres_validate(a["prefix"], a["delta"], a["blocks"], a["ts"], a["ss"], a["cap"],
+                                    a["nb"], a["res_w"], a["rms_w"], a["eps"], a["onw"], a["oeps"],
+                                    a["widx"], a["out"], a["T"], a["H"])
+
+
+CASES = [
+    ("valid", {}, "ATTNRES_OK"),
+    ("valid_no_optional", dict(delta=None, onw=None, widx=-1), "ATTNRES_OK"),
+    ("valid_nb0_no_bank", dict(nb=0, blocks=None, widx=-1), "ATTNRES_OK"),
+    ("valid_write_last_slot", dict(widx=7), "ATTNRES_OK"),
+    ("valid_padded_token_stride", dict(ts=8 * H + 64), "ATTNRES_OK"),
+    ("valid_slot_major", dict(ts=H, ss=4 * H), "ATTNRES_OK"),
+    ("valid_single_token_any_token_stride", dict(T=1, ts=0), "ATTNRES_OK"),
+    ("valid_empty", dict(T=0, prefix=None, out=None), "ATTNRES_OK"),
+    ("null_prefix", dict(prefix=None), "ATTNRES_E_NULL"),
+    ("null_out", dict(out=None), "ATTNRES_E_NULL"),
+    ("null_res_w", dict(res_w=None), "ATTNRES_E_NULL"),
+    ("null_rms_w", dict(rms_w=None), "ATTNRES_E_NULL"),
+    ("null_bank_with_blocks", dict(blocks=None), "ATTNRES_E_NULL"),
+    ("null_bank_with_write", dict(nb=0, blocks=None, widx=0), "ATTNRES_E_NULL"),
+    ("negative_T", dict(T=-1), "ATTNRES_E_SHAPE"),
+    ("zero_H", dict(H=0), "ATTNRES_E_SHAPE"),
+    ("negative_capacity", dict(cap=-1, nb=0), "ATTNRES_E_SHAPE"),
+    ("too_many_tokens", dict(T=1 << 31), "ATTNRES_E_SHAPE"),
+    ("huge_stride", dict(ts=1 << 50), "ATTNRES_E_SHAPE"),
+    ("other_hidden_size", dict(H=4096), "ATTNRES_E_UNSUPPORTED"),
+    ("nb_negative", dict(nb=-1), "ATTNRES_E_NUM_BLOCKS"),
+    ("nb_above_8", dict(nb=9, cap=10, ts=10 * H), "ATTNRES_E_NUM_BLOCKS"),
+    ("nb_above_capacity", dict(nb=5, cap=4, ts=4 * H), "ATTNRES_E_NUM_BLOCKS"),
+    ("widx_below_minus_one", dict(widx=-2), "ATTNRES_E_WRITE_IDX"),
+    ("widx_at_capacity", dict(widx=8), "ATTNRES_E_WRITE_IDX"),
+    ("eps_negative", dict(eps=-1e-6), "ATTNRES_E_EPS"),
+    ("eps_nan", dict(eps=float("nan")), "ATTNRES_E_EPS"),
+    ("eps_inf", dict(eps=float("inf")), "ATTNRES_E_EPS"),
+    ("out_eps_negative", dict(oeps=-1.0), "ATTNRES_E_EPS"),
+    ("misaligned_prefix", dict(prefix=0x10000008), "ATTNRES_E_ALIGN"),
+    ("misaligned_delta", dict(delta=0x20000002), "ATTNRES_E_ALIGN"),
+    ("misaligned_bank", dict(blocks=0x40000004), "ATTNRES_E_ALIGN"),
+    ("misaligned_weight", dict(onw=0x30200008), "ATTNRES_E_ALIGN"),
+    ("misaligned_out", dict(out=0x50000002), "ATTNRES_E_ALIGN"),
+    ("token_stride_not_multiple_of_8", dict(ts=8 * H + 4), "ATTNRES_E_ALIGN"),
+    ("negative_stride", dict(ss=-H), "ATTNRES_E_STRIDE"),
+    ("slot_stride_overlaps_rows", dict(ss=H - 8), "ATTNRES_E_STRIDE"),
+    ("token_stride_overlaps_slots", dict(ts=7 * H), "ATTNRES_E_STRIDE"),
+    ("zero_strides", dict(ts=0, ss=0), "ATTNRES_E_STRIDE"),
+    ("out_aliases_prefix", dict(out=0x10000000), "ATTNRES_E_ALIAS"),
+    ("out_overlaps_prefix_tail", dict(out=0x10000000 + 2 * H * 3), "ATTNRES_E_ALIAS"),
+    ("out_inside_bank", dict(out=0x40000000 + 2 * H * 9), "ATTNRES_E_ALIAS"),
+    ("out_on_weight", dict(out=0x30100000), "ATTNRES_E_ALIAS"),
+    ("prefix_written_over_delta", dict(delta=0x10000000 + 32), "ATTNRES_E_ALIAS"),
+    ("bank_written_over_prefix", dict(widx=2, prefix=0x40000000 + 2 * H * 8), "ATTNRES_E_ALIAS"),
+    ("bank_written_over_weight", dict(widx=2, res_w=0x40000000 + 2 * H * 17), "ATTNRES_E_ALIAS"),
+]
+
+
+@pytest.mark.parametrize("name,mod,expect", CASES, ids=[c[0] for c in CASES])
+def test_validate(A, name, mod, expect):
+    rc = _validate(A, _args(**mod))
+    assert A.STATUS[rc] == expect
+
+
+def test_read_only_overlaps_are_allowed(A):
+    # prefix read-only (no delta) may share memory with a read-only bank and
+    # with the weights; only written buffers must be exclusive.
+    a = _args(delta=None, widx=-1, res_w=0x10000000, rms_w=0x10000000)
+    assert _validate(A, a) == 0
+
+
+def test_fwd_rejects_before_any_gpu_work(A):
+    """attnres_fwd runs the same checks first: an invalid call returns its
+    code without touching the (fake) pointers or needing a GPU."""
+    a = _args(H=4096)
+    lib = A.lib()
+    for fn, extra in ((lib.attnres_fwd, [None]), (lib.attnres_fwd_path, [None, A.ATTNRES_PATH_ROW])):
+        rc = fn(a["prefix"], a["delta"], a["blocks"], a["ts"], a["ss"], a["cap"], a["nb"], a["res_w"],
+                a["rms_w"], a["eps"], a["onw"], a["oeps"], a["widx"], a["out"], a["T"], a["H"], *extra)
+        assert A.STATUS[rc] == "ATTNRES_E_UNSUPPORTED"
+    a = _args()
+    rc = lib.attnres_fwd_path(a["prefix"], a["delta"], a["blocks"], a["ts"], a["ss"], a["cap"], a["nb"],
+                              a["res_w"], a["rms_w"], a["eps"], a["onw"], a["oeps"], a["widx"], a["out"],
+                              a["T"], a["H"], None, 7)
+    assert A.STATUS[rc] == "ATTNRES_E_PATH"
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package and its native sources do not import, load or name the
+    oracle (only tests, the smoke check and the benchmark's CPU leg may)."""
+    pkg = os.path.join(ROOT, "kimi_k3_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"(import\s+oracle|from\s+oracle|liboracle|oracle_attnres|oracle\.)",
+                                     text), f"{f} uses the oracle"
