@@ -37,6 +37,21 @@
 
 #include "attnres_internal.h"
 
+// Tuning knobs, fixed at compile time.  Every setting computes the full
+// result; they only change occupancy, grid shape and cache policy.
+#ifndef ATTNRES_ROW_MAX_VGPRS
+#define ATTNRES_ROW_MAX_VGPRS 128       // <= 128: 4 waves/SIMD, so two 7-wave workgroups
+#endif                                  // fit a CU however its waves spread over SIMDs
+#ifndef ATTNRES_ROW_WGS_PER_CU
+#define ATTNRES_ROW_WGS_PER_CU 0        // 0: one workgroup per token; k: k per CU, looping
+#endif
+#ifndef ATTNRES_NT_LOADS
+#define ATTNRES_NT_LOADS 1              // streaming rows read non-temporally
+#endif
+#ifndef ATTNRES_NT_STORES
+#define ATTNRES_NT_STORES 1             // streaming rows written non-temporally
+#endif
+
 namespace attnres {
 namespace {
 
@@ -47,8 +62,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kSeg = 8;                       // bf16 per 16-byte segment
 constexpr int kSegs = kHidden / kSeg;         // 896 segments per row
 constexpr int kWave = 64;
-constexpr int kRowThreads = kSegs;            // row path: one segment per lane
-constexpr int kRowWaves = kRowThreads / kWave;  // 14
+constexpr int kRowSegsPerLane = 2;           // row path: two segments per lane
+constexpr int kRowThreads = kSegs / kRowSegsPerLane;  // 448 = 7 waves
+constexpr int kRowWaves = kRowThreads / kWave;        // 7
 constexpr int kParts = 14;                    // split path: workgroups per token
 constexpr int kPartThreads = kSegs / kParts;  // 64 = one wave
 constexpr int kSlot = 20;                     // floats per (token, part) workspace slot
@@ -59,7 +75,8 @@ constexpr int kAutoSplitMaxTokens = 32;       // attnres_fwd uses the split path
 constexpr float kInvHidden = 1.0f / kHidden;
 
 static_assert(kSegs * kSeg == kHidden, "hidden size must be a multiple of 8");
-static_assert(kRowThreads % kWave == 0, "row workgroup must be whole waves");
+static_assert(kRowThreads % kWave == 0 && kRowThreads * kRowSegsPerLane == kSegs,
+              "row workgroup must be whole waves covering the row");
 static_assert(kPartThreads == kWave, "a split part is one wave");
 static_assert(2 * (kMaxBlocks + 1) < kSlotYsq, "workspace slot too small");
 
@@ -89,13 +106,21 @@ struct KParams {
 // Streaming rows are touched exactly once: non-temporal 128-bit accesses keep
 // them from evicting the weights, which every workgroup re-reads from L2.
 __device__ __forceinline__ u32x4 load_stream(const uint16_t *p) {
+#if ATTNRES_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+#else
+  return *reinterpret_cast<const u32x4 *>(p);
+#endif
 }
 __device__ __forceinline__ u32x4 load_cached(const uint16_t *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 __device__ __forceinline__ void store_stream(uint16_t *p, u32x4 v) {
+#if ATTNRES_NT_STORES
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+#else
+  *reinterpret_cast<u32x4 *>(p) = v;
+#endif
 }
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32.
@@ -109,73 +134,95 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// acc + a.lo * b.lo + a.hi * b.hi on packed bf16 pairs, fp32 accumulate
+// (v_dot2c_f32_bf16): the products of bf16 values are exact in fp32.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ float dpp_src(float v) {
   return __int_as_float(
       __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
 }
 
-// Sum over the 64 lanes of a wave; the total is valid in lane 63.  Butterfly
-// inside each 16-lane row (xor 1, xor 2, half-row mirror, row mirror: every
-// lane of a row then holds the row sum), then row 0 is folded into row 1 and
-// row 2 into row 3 (broadcast of lane 15 / 47), then rows 0+1 into row 3
-// (broadcast of lane 31).  The order is fixed, so results are repeatable.
-__device__ __forceinline__ float wave_sum_lane63(float v) {
-  v += dpp_src<0xB1>(v);        // quad_perm [1,0,3,2]
-  v += dpp_src<0x4E>(v);        // quad_perm [2,3,0,1]
-  v += dpp_src<0x141>(v);       // row_half_mirror
-  v += dpp_src<0x140>(v);       // row_mirror
-  v += dpp_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v += dpp_src<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+// Butterfly sum inside each 16-lane row of a wave (xor 1, xor 2, half-row
+// mirror, row mirror): afterwards every lane of a row holds its row's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_src<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_src<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_src<0x141>(v);  // row_half_mirror
+  v += dpp_src<0x140>(v);  // row_mirror
   return v;
 }
 
-// Hides the packed rows from the optimiser between the reduction and the
-// mixture, so it keeps 4 packed words per row live instead of 8 unpacked
-// fp32 values (the unpack is one shift or mask per element, cheaper than the
-// occupancy the extra registers would cost).  Emits no instruction.
-template <int NS>
-__device__ __forceinline__ void keep_packed(u32x4 (&x)[NS]) {
-#pragma unroll
-  for (int j = 0; j < NS; ++j) asm volatile("" : "+v"(x[j]));
+// Sum over the 64 lanes of a wave, valid in lane 63: the row sums, then row 0
+// folded into row 1 and row 2 into row 3 (broadcast of lanes 15 / 47), then
+// rows 0+1 into row 3 (broadcast of lane 31).  Fixed order: repeatable.
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  v = row16_sum(v);
+  v += dpp_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_src<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Everything one lane reads, issued in one burst: the L2-resident weights
-// first (the wait counter is in order, so the query can be formed while the
-// rows are still in flight), then the bank rows, prefix and delta.  Row bases
-// are workgroup-uniform (scalar registers); the lane adds its 16-byte segment
-// offset.
-template <int NB, bool DELTA, bool ONORM>
-struct TokenLoads {
-  u32x4 rms, res, onw;  // weights
-  u32x4 x[NB + 1];      // bank slots 0..NB-1, then prefix (cur after finish_cur)
-  u32x4 d;              // delta
+// One token's data for SPL segments per lane: segment i of this lane is
+// seg0 + i * seg_step.  Everything is issued in one burst: the L2-resident
+// weights first (the wait counter is in order, so the query can be formed
+// while the rows are still in flight), then the bank rows, prefix and delta.
+// Row bases are workgroup-uniform (scalar registers); lanes add their
+// 16-byte segment offsets.
+template <int NB, bool DELTA, bool ONORM, int SPL>
+struct Token {
+  static constexpr int NS = NB + 1;
+  u32x4 rms[SPL], res[SPL], onw[SPL];  // weights
+  u32x4 x[NS][SPL];                    // bank slots 0..NB-1, then prefix (cur after finish_cur)
+  u32x4 d[SPL];                        // delta
 
-  __device__ __forceinline__ void issue(const KParams &p, int64_t t, int seg) {
-    const int off = seg * kSeg;
-    rms = load_cached(p.rms_w + off);
-    res = load_cached(p.res_w + off);
-    if constexpr (ONORM) onw = load_cached(p.onw + off);
+  __device__ __forceinline__ void issue(const KParams &p, int64_t t, int seg0, int seg_step) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int off = (seg0 + i * seg_step) * kSeg;
+      rms[i] = load_cached(p.rms_w + off);
+      res[i] = load_cached(p.res_w + off);
+      if constexpr (ONORM) onw[i] = load_cached(p.onw + off);
+    }
     const uint16_t *bank = p.blocks + t * p.tok_stride;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) x[j] = load_stream(bank + j * p.slot_stride + off);
-    x[NB] = load_stream(p.prefix + t * kHidden + off);
-    if constexpr (DELTA) d = load_stream(p.delta + t * kHidden + off);
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int i = 0; i < SPL; ++i)
+        x[j][i] = load_stream(bank + j * p.slot_stride + (seg0 + i * seg_step) * kSeg);
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      x[NB][i] = load_stream(p.prefix + t * kHidden + (seg0 + i * seg_step) * kSeg);
+    if constexpr (DELTA)
+#pragma unroll
+      for (int i = 0; i < SPL; ++i)
+        d[i] = load_stream(p.delta + t * kHidden + (seg0 + i * seg_step) * kSeg);
     // Keep the scheduler from sinking any of these loads below the arithmetic.
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Fused query q = rms_w * res_w for this lane's 8 elements (exact in fp32).
-  __device__ __forceinline__ void query(float (&q)[8]) const {
+  // Fused query q = rms_w * res_w, split exactly into two packed bf16 words:
+  // q has at most 16 significant bits (a product of two 8-bit significands),
+  // so q_hi = bf16_RNE(q) and the residual q_lo = q - q_hi (computed exactly
+  // in fp32) is itself a bf16 value, and q = q_hi + q_lo.
+  __device__ __forceinline__ void query(u32x4 (&qh)[SPL], u32x4 (&ql)[SPL]) const {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      q[2 * k] = bf_lo(rms[k]) * bf_lo(res[k]);
-      q[2 * k + 1] = bf_hi(rms[k]) * bf_hi(res[k]);
-    }
+    for (int i = 0; i < SPL; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a = bf_lo(rms[i][k]) * bf_lo(res[i][k]);
+        const float b = bf_hi(rms[i][k]) * bf_hi(res[i][k]);
+        qh[i][k] = pack_bf16x2(a, b);
+        ql[i][k] = pack_bf16x2(a - bf_lo(qh[i][k]), b - bf_hi(qh[i][k]));
+      }
   }
 
   // cur = bf16_RNE(prefix + delta) into x[NB].  The fp32 sum of two bf16
@@ -184,160 +231,201 @@ struct TokenLoads {
   __device__ __forceinline__ void finish_cur() {
     if constexpr (DELTA) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        x[NB][k] = pack_bf16x2(bf_lo(x[NB][k]) + bf_lo(d[k]), bf_hi(x[NB][k]) + bf_hi(d[k]));
+      for (int i = 0; i < SPL; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          x[NB][i][k] = pack_bf16x2(bf_lo(x[NB][i][k]) + bf_lo(d[i][k]),
+                                    bf_hi(x[NB][i][k]) + bf_hi(d[i][k]));
+    }
+  }
+
+  // Per-lane partial sum of squares and query dot of every source.
+  __device__ __forceinline__ void partials(const u32x4 (&qh)[SPL], const u32x4 (&ql)[SPL],
+                                           float (&ss)[NS], float (&dq)[NS]) const {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      float s = 0.f, dd = 0.f;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          s = dot2(x[j][i][k], x[j][i][k], s);
+          dd = dot2(qh[i][k], x[j][i][k], dd);
+          dd = dot2(ql[i][k], x[j][i][k], dd);
+        }
+      ss[j] = s;
+      dq[j] = dd;
+    }
+  }
+
+  // Hides the packed rows from the optimiser between the reduction and the
+  // mixture, so it keeps the packed words live rather than unpacked fp32
+  // copies.  Emits no instruction.
+  __device__ __forceinline__ void keep_packed() {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) asm volatile("" : "+v"(x[j][i]));
+  }
+
+  // y = sum_j p_j x_j over the raw rows, fp32; p_j is read from lane j as a
+  // scalar operand.
+  __device__ __forceinline__ void mix(float p_lane, float (&y)[SPL][8]) const {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[i][k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float pj = lane_value(p_lane, j);
+#pragma unroll
+      for (int i = 0; i < SPL; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          y[i][2 * k] = fmaf(pj, bf_lo(x[j][i][k]), y[i][2 * k]);
+          y[i][2 * k + 1] = fmaf(pj, bf_hi(x[j][i][k]), y[i][2 * k + 1]);
+        }
+    }
+  }
+
+  // out = bf16_RNE(y * rsig * w) (or y), then the in-place writes of cur,
+  // after every read of this lane's elements.
+  __device__ __forceinline__ void store(const KParams &p, int64_t t, int seg0, int seg_step,
+                                        const float (&y)[SPL][8], float rsig) const {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int64_t off = int64_t(seg0 + i * seg_step) * kSeg;
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (ONORM)
+          o[k] = pack_bf16x2(y[i][2 * k] * rsig * bf_lo(onw[i][k]),
+                             y[i][2 * k + 1] * rsig * bf_hi(onw[i][k]));
+        else
+          o[k] = pack_bf16x2(y[i][2 * k], y[i][2 * k + 1]);
+      }
+      store_stream(p.out + t * kHidden + off, o);
+      if constexpr (DELTA) store_stream(p.prefix + t * kHidden + off, x[NB][i]);
+      if (p.widx >= 0)
+        store_stream(p.blocks + t * p.tok_stride + p.widx * p.slot_stride + off, x[NB][i]);
     }
   }
 };
 
-// Per-lane partial sum of squares and query dot of one source row segment.
-__device__ __forceinline__ void row_partials(const u32x4 &x, const float (&q)[8], float &ss,
-                                             float &dq) {
-  float s = 0.f, d = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float a = bf_lo(x[k]), b = bf_hi(x[k]);
-    s = fmaf(a, a, s);
-    s = fmaf(b, b, s);
-    d = fmaf(q[2 * k], a, d);
-    d = fmaf(q[2 * k + 1], b, d);
-  }
-  ss = s;
-  dq = d;
-}
-
-// Softmax weights of the NS sources.  Lane j (< NS) holds logit j.  The
-// normaliser is accumulated in online form (running max m, running sum z of
-// exp(l - m), rescaled whenever the max moves); every lane computes the same
-// uniform values.
-template <int NS>
-__device__ __forceinline__ void softmax_weights(float logit_lane, float (&pw)[NS]) {
-  float l[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) l[j] = lane_value(logit_lane, j);
-  float m = l[0], z = 1.f;
-#pragma unroll
-  for (int j = 1; j < NS; ++j) {
-    const float mn = fmaxf(m, l[j]);
-    z = z * __expf(m - mn) + __expf(l[j] - mn);
-    m = mn;
-  }
-  const float inv = 1.f / z;
-#pragma unroll
-  for (int j = 0; j < NS; ++j) pw[j] = __expf(l[j] - m) * inv;
-}
-
-// y = sum_j p_j x_j over the raw rows, fp32.
-template <int NS>
-__device__ __forceinline__ void mix(const u32x4 (&x)[NS], const float (&pw)[NS], float (&y)[8]) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = 0.f;
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      y[2 * k] = fmaf(pw[j], bf_lo(x[j][k]), y[2 * k]);
-      y[2 * k + 1] = fmaf(pw[j], bf_hi(x[j][k]), y[2 * k + 1]);
-    }
-  }
-}
-
-__device__ __forceinline__ float sum_sq8(const float (&y)[8]) {
+template <int SPL>
+__device__ __forceinline__ float sum_sq(const float (&y)[SPL][8]) {
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) s = fmaf(y[k], y[k], s);
+  for (int i = 0; i < SPL; ++i)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s = fmaf(y[i][k], y[i][k], s);
   return s;
 }
 
-template <bool ONORM>
-__device__ __forceinline__ void store_token(const KParams &p, int64_t t, int seg, const float (&y)[8],
-                                            float rsig, const u32x4 &w) {
-  const int64_t h0 = int64_t(seg) * kSeg;
-  u32x4 o;
-  if constexpr (ONORM) {
+// Softmax over the NS sources.  Lane j (< NS) holds logit j; lane j of the
+// result holds p_j.  The normaliser is accumulated in online form (running
+// max m and running sum z of exp(l - m), rescaled whenever the max moves) on
+// wave-uniform values, identically in every wave.
+template <int NS>
+__device__ __forceinline__ float softmax_lanes(float logit_lane) {
+  float m = lane_value(logit_lane, 0), z = 1.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      o[k] = pack_bf16x2(y[2 * k] * rsig * bf_lo(w[k]), y[2 * k + 1] * rsig * bf_hi(w[k]));
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
+  for (int j = 1; j < NS; ++j) {
+    const float l = lane_value(logit_lane, j);
+    const float mn = fmaxf(m, l);
+    z = z * __expf(m - mn) + __expf(l - mn);
+    m = mn;
   }
-  store_stream(p.out + t * kHidden + h0, o);
-}
-
-// In-place writes of cur, after every read of this lane's elements.
-template <bool DELTA>
-__device__ __forceinline__ void store_cur(const KParams &p, int64_t t, int seg, const u32x4 &cur) {
-  const int64_t h0 = int64_t(seg) * kSeg;
-  if constexpr (DELTA) store_stream(p.prefix + t * kHidden + h0, cur);
-  if (p.widx >= 0) store_stream(p.blocks + t * p.tok_stride + p.widx * p.slot_stride + h0, cur);
+  return __expf(logit_lane - m) * (1.f / z);
 }
 
 // ---------------------------------------------------------------------------
-// row path: one workgroup per token
+// row path: one workgroup (7 waves, two segments per lane) per token
 // ---------------------------------------------------------------------------
 
+constexpr int kRowRows = kRowWaves * 4;  // 16-lane row partials per workgroup
+
+// Sums the kRowRows row partials of one value in a fixed order.
+__device__ __forceinline__ float sum_row_partials(const float *v) {
+  const float4 *v4 = reinterpret_cast<const float4 *>(v);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRowRows / 4; ++i) {
+    const float4 a = v4[i];
+    s += a.x;
+    s += a.y;
+    s += a.z;
+    s += a.w;
+  }
+  return s;
+}
+
+// The grid either has one workgroup per token or is persistent (a few
+// workgroups per CU looping over tokens); LDS partials are double-buffered by
+// iteration parity so one barrier per phase suffices.
 template <int NB, bool DELTA, bool ONORM>
-__global__ void __launch_bounds__(kRowThreads) attnres_row_kernel(KParams p) {
+__global__ void __attribute__((amdgpu_flat_work_group_size(kRowThreads, kRowThreads),
+                               // the unified arch+acc register file counts double
+                               amdgpu_num_vgpr(ATTNRES_ROW_MAX_VGPRS / 2)))
+attnres_row_kernel(KParams p) {
   constexpr int NS = NB + 1;
-  __shared__ float s_red[kRowWaves][2 * NS];
-  __shared__ float s_ysq[kRowWaves];
+  constexpr int SPL = kRowSegsPerLane;
+  __shared__ __align__(16) float s_part[2][2 * NS][kRowRows];
+  __shared__ __align__(16) float s_ysq[2][kRowRows];
 
-  const int64_t t = blockIdx.x;
-  const int seg = threadIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
+  const int rowslot = wave * 4 + (lane >> 4);  // this lane's 16-lane row in the workgroup
+  const bool row_leader = (lane & 15) == 0;
 
-  TokenLoads<NB, DELTA, ONORM> in;
-  in.issue(p, t, seg);
-  float q[8];
-  in.query(q);
-  in.finish_cur();
-  u32x4 (&x)[NS] = in.x;
+  // One token per workgroup unless the grid is persistent; a loop the
+  // compiler cannot see through would hoist the weights and cost registers.
+  constexpr bool kLoop = ATTNRES_ROW_WGS_PER_CU > 0;
+  const int64_t t_step = kLoop ? int64_t(gridDim.x) : p.T;
+  int par = 0;
+  for (int64_t t = blockIdx.x; t < p.T; t += t_step, par ^= 1) {
+    Token<NB, DELTA, ONORM, SPL> tk;
+    tk.issue(p, t, threadIdx.x, kRowThreads);
+    u32x4 qh[SPL], ql[SPL];
+    tk.query(qh, ql);
+    tk.finish_cur();
 
-  // Each source is reduced and published as soon as its partials exist, so
-  // only two partial sums are live at a time.
+    float ss[NS], dq[NS];
+    tk.partials(qh, ql, ss, dq);
+    tk.keep_packed();
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    float s, d;
-    row_partials(x[j], q, s, d);
-    s = wave_sum_lane63(s);
-    d = wave_sum_lane63(d);
-    if (lane == kWave - 1) {
-      s_red[wave][j] = s;
-      s_red[wave][NS + j] = d;
+    for (int j = 0; j < NS; ++j) {
+      ss[j] = row16_sum(ss[j]);
+      dq[j] = row16_sum(dq[j]);
     }
-  }
-  keep_packed<NS>(x);
-  __syncthreads();
-
-  float logit = 0.f;
-  if (lane < NS) {
-    float s = 0.f, d = 0.f;
+    if (row_leader) {
 #pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) {
-      s += s_red[w][lane];
-      d += s_red[w][NS + lane];
+      for (int j = 0; j < NS; ++j) {
+        s_part[par][j][rowslot] = ss[j];
+        s_part[par][NS + j][rowslot] = dq[j];
+      }
     }
-    logit = d * rsqrtf(s * kInvHidden + p.rms_eps);
-  }
-  float pw[NS];
-  softmax_weights<NS>(logit, pw);
-  float y[8];
-  mix<NS>(x, pw, y);
-
-  float rsig = 1.f;
-  if constexpr (ONORM) {
-    const float sy = wave_sum_lane63(sum_sq8(y));
-    if (lane == kWave - 1) s_ysq[wave] = sy;
     __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) tot += s_ysq[w];
-    rsig = rsqrtf(tot * kInvHidden + p.out_eps);
+
+    float logit = 0.f;
+    if (lane < NS) {
+      const float s = sum_row_partials(s_part[par][lane]);
+      const float d = sum_row_partials(s_part[par][NS + lane]);
+      logit = d * rsqrtf(s * kInvHidden + p.rms_eps);
+    }
+    const float p_lane = softmax_lanes<NS>(logit);
+    float y[SPL][8];
+    tk.mix(p_lane, y);
+
+    float rsig = 1.f;
+    if constexpr (ONORM) {
+      const float sy = row16_sum(sum_sq<SPL>(y));
+      if (row_leader) s_ysq[par][rowslot] = sy;
+      __syncthreads();
+      rsig = rsqrtf(sum_row_partials(s_ysq[par]) * kInvHidden + p.out_eps);
+    }
+    tk.store(p, t, threadIdx.x, kRowThreads, y, rsig);
   }
-  store_token<ONORM>(p, t, seg, y, rsig, in.onw);
-  store_cur<DELTA>(p, t, seg, x[NB]);
 }
 
 // ---------------------------------------------------------------------------
@@ -372,31 +460,32 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   const int64_t t = blockIdx.x / kParts;
   const int part = blockIdx.x - int(t) * kParts;
   const int lane = threadIdx.x;
-  const int seg = part * kPartThreads + lane;
 
-  TokenLoads<NB, DELTA, ONORM> in;
-  in.issue(p, t, seg);
-  float q[8];
-  in.query(q);
-  in.finish_cur();
-  u32x4 (&x)[NS] = in.x;
+  Token<NB, DELTA, ONORM, 1> tk;
+  tk.issue(p, t, part * kPartThreads + lane, 0);
+  u32x4 qh[1], ql[1];
+  tk.query(qh, ql);
+  tk.finish_cur();
 
-  float *const tok_ws = p.ws_part + size_t(t) * kParts * kSlot;
-  unsigned long long *const cnt = p.ws_count + size_t(t) * kCounterStride;
-  float *const slot = tok_ws + part * kSlot;
+  float ss[NS], dq[NS];
+  tk.partials(qh, ql, ss, dq);
+  tk.keep_packed();
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    float s, d;
-    row_partials(x[j], q, s, d);
-    s = wave_sum_lane63(s);
-    d = wave_sum_lane63(d);
-    if (lane == kWave - 1) {
-      slot[j] = s;
-      slot[NS + j] = d;
-    }
+    ss[j] = wave_sum_lane63(ss[j]);
+    dq[j] = wave_sum_lane63(dq[j]);
   }
-  keep_packed<NS>(x);
-  if (lane == kWave - 1) arrive_and_wait(cnt, p.ws_flag);
+  float *const tok_ws = p.ws_part + size_t(t) * kParts * kSlot;
+  unsigned long long *const cnt = p.ws_count + size_t(t) * kCounterStride;
+  if (lane == kWave - 1) {
+    float *const slot = tok_ws + part * kSlot;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      slot[j] = ss[j];
+      slot[NS + j] = dq[j];
+    }
+    arrive_and_wait(cnt, p.ws_flag);
+  }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   float logit = 0.f;
@@ -409,14 +498,13 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     }
     logit = d * rsqrtf(s * kInvHidden + p.rms_eps);
   }
-  float pw[NS];
-  softmax_weights<NS>(logit, pw);
-  float y[8];
-  mix<NS>(x, pw, y);
+  const float p_lane = softmax_lanes<NS>(logit);
+  float y[1][8];
+  tk.mix(p_lane, y);
 
   float rsig = 1.f;
   if constexpr (ONORM) {
-    const float sy = wave_sum_lane63(sum_sq8(y));
+    const float sy = wave_sum_lane63(sum_sq<1>(y));
     if (lane == kWave - 1) {
       tok_ws[part * kSlot + kSlotYsq] = sy;
       arrive_and_wait(cnt, p.ws_flag);
@@ -427,8 +515,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     for (int r = 0; r < kParts; ++r) tot += load_agent(tok_ws + r * kSlot + kSlotYsq);
     rsig = rsqrtf(tot * kInvHidden + p.out_eps);
   }
-  store_token<ONORM>(p, t, seg, y, rsig, in.onw);
-  store_cur<DELTA>(p, t, seg, x[NB]);
+  tk.store(p, t, part * kPartThreads + lane, 0, y, rsig);
 }
 
 // ---------------------------------------------------------------------------
@@ -557,7 +644,16 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
 
   KernelFn fn = pick(split, a.num_blocks, a.delta != nullptr, a.output_norm_weight != nullptr);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;
-  const dim3 grid = split ? dim3(unsigned(a.T) * kParts) : dim3(unsigned(a.T));
+  unsigned row_grid = unsigned(a.T);
+  if (!split && ATTNRES_ROW_WGS_PER_CU > 0) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    const int64_t cap = int64_t(cus) * ATTNRES_ROW_WGS_PER_CU;
+    if (a.T > cap) row_grid = unsigned(cap);
+  }
+  const dim3 grid = split ? dim3(unsigned(a.T) * kParts) : dim3(row_grid);
   const dim3 block = split ? dim3(kPartThreads) : dim3(kRowThreads);
   void *args[] = {&kp};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, args, 0, s);
