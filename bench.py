@@ -38,7 +38,9 @@ METRIC = "AttnRes µs/call (T=1, 0/4/8 blk) + achieved HBM GB/s at T=1024, 8 blk
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 DOMINANT_KERNEL = "attnres_row_kernel<8, true, true>"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_kernel_mid_prefill.json")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "attnres_row_kernel_mid_prefill_T1024_traffic.json")
+CALIBRATION_BYTES = 512 << 20
 KERNEL_SOURCES = [os.path.join(ROOT, "kimi_k3_attention_amd", "csrc", f)
                   for f in ("attnres_kernels.hip", "attnres_internal.h")]
 
@@ -132,7 +134,7 @@ def pct(xs, q):
     return float(np.percentile(np.asarray(xs), q))
 
 
-def calibration_copy(nbytes: int = 512 << 20, reps: int = 3):
+def calibration_copy(nbytes: int = CALIBRATION_BYTES, reps: int = 3):
     """A plain device copy of known size, for scaling the memory-traffic
     counters (FETCH_SIZE / WRITE_SIZE) of the same profiling run."""
     src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
@@ -215,7 +217,7 @@ def cpu_baseline(target_s: float = 10.0):
                        f"{dt * 1e3:.0f} ms/call")
 
 
-def load_traffic(per_call_ms):
+def load_traffic():
     """HBM bytes per launch from the committed counter runs, if they were taken
     on the current kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -227,6 +229,84 @@ def load_traffic(per_call_ms):
     return t.get("bytes_per_launch")
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (run on the CSV output of the profiling commands)
+# ---------------------------------------------------------------------------
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(names)
+
+
+def write_kernel_stats(trace_dir, out_name, title, command):
+    """profiles/<out_name>: the kernel-trace statistics of one profiling run."""
+    os.makedirs(PROFILES, exist_ok=True)
+    lines = [f"# rocprofv3 kernel statistics, {title}", f"# command: {command}",
+             f"# kernel source hash: {kernel_source_hash()}",
+             "# name | calls | average us | min us | max us | share %"]
+    for r in _csv_rows(trace_dir, "kernel_stats.csv"):
+        lines.append(" | ".join([_col(r, "Name", "KernelName")[:90], _col(r, "Calls"),
+                                 f"{float(_col(r, 'AverageNs')) / 1e3:.3f}",
+                                 f"{float(_col(r, 'MinNs')) / 1e3:.3f}", f"{float(_col(r, 'MaxNs')) / 1e3:.3f}",
+                                 f"{float(_col(r, 'Percentage')):.2f}"]))
+    with open(os.path.join(PROFILES, out_name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_profile(trace_dir, fetch_dir, write_dir, commands):
+    """Writes the committed profiles/ summaries: the kernel-trace statistics
+    and the HBM traffic per launch of the dominant kernel, scaled by what the
+    same counters read for the plain copy of known size in the same run."""
+    os.makedirs(PROFILES, exist_ok=True)
+    src_hash = kernel_source_hash()
+    write_kernel_stats(trace_dir, "attnres_row_kernel_mid_prefill_T1024_kernel_stats.txt",
+                       "mid prefill T=1024 nb=8 (hipGraph replay)", commands.get("trace", "?"))
+
+    def per_kernel(rows):
+        out = {}
+        for r in rows:
+            name = _col(r, "Kernel_Name", "Kernel-Name", "KernelName")
+            grid = int(float(_col(r, "Grid_Size", "Grid-Size", "GridSize")))
+            val = float(_col(r, "Counter_Value", "Counter-Value", "CounterValue"))
+            out.setdefault((name, grid), []).append(val)
+        return out
+
+    res = {}
+    for tag, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        pk = per_kernel(_csv_rows(d, "counter_collection.csv"))
+        ours = [v for (n, g), vals in pk.items() if "attnres_row_kernel<8, true, true>" in n for v in vals]
+        # the calibration copy: the kernel whose counter reads about the copy size
+        calib = [(n, g, float(np.median(v))) for (n, g), v in pk.items()
+                 if "attnres" not in n and len(v) >= 3]
+        calib = max(calib, key=lambda x: x[2])
+        factor = (CALIBRATION_BYTES / 1024) / calib[2]
+        res[tag] = dict(kernel_kib_median=float(np.median(ours)), dispatches=len(ours),
+                        calibration_kernel=calib[0][:60], calibration_kib=calib[2],
+                        calibration_known_kib=CALIBRATION_BYTES / 1024, scale=factor,
+                        bytes_per_launch=float(np.median(ours)) * 1024 * factor)
+    case = W.mid_prefill()
+    total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    out = dict(workload="mid prefill T=1024 nb=8 H=7168 delta+onorm widx=3", kernel=DOMINANT_KERNEL,
+               kernel_source_hash=src_hash, commands=commands, counters=res,
+               bytes_per_launch=round(total), algorithmic_bytes_per_launch=case.algorithmic_bytes(),
+               ratio_to_algorithmic=round(total / case.algorithmic_bytes(), 4))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,7 +316,18 @@ def main():
     ap.add_argument("--only", choices=["mid", "decode"], default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--calibrate", action="store_true", help="run the known-size copy for counters")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output directories")
+    ap.add_argument("--profile-commands", default=None, help="JSON of the commands that made them")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT_NAME", "TITLE", "COMMAND"),
+                    help="write one kernel-statistics summary into profiles/")
     args = ap.parse_args()
+    if args.summarize_trace:
+        write_kernel_stats(*args.summarize_trace)
+        return
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile, commands=json.loads(args.profile_commands or "{}"))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the attention-residual op shards by tokens with no exchange, so the "
@@ -274,7 +365,7 @@ def main():
             "roofline": {"bound": "hbm", "kernel": DOMINANT_KERNEL, "achieved": round(achieved, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                         "traffic": load_traffic(mid["per_call_ms"]),
+                         "traffic": load_traffic(),
                          "algorithmic_bytes_per_launch": mid["bytes"]},
             "mid_prefill_us_per_call": {k: round(v, 3) for k, v in mid["us"].items()},
         })

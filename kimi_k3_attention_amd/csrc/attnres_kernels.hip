@@ -45,6 +45,12 @@
 #ifndef ATTNRES_ROW_WGS_PER_CU
 #define ATTNRES_ROW_WGS_PER_CU 0        // 0: one workgroup per token; k: k per CU, looping
 #endif
+#ifndef ATTNRES_COUNTER_STRIDE_BYTES
+#define ATTNRES_COUNTER_STRIDE_BYTES 128  // spacing of the split path's per-token counters
+#endif
+#ifndef ATTNRES_SPIN_SLEEP
+#define ATTNRES_SPIN_SLEEP 1              // s_sleep argument between polls (x64 cycles)
+#endif
 #ifndef ATTNRES_NT_LOADS
 #define ATTNRES_NT_LOADS 1              // streaming rows read non-temporally
 #endif
@@ -69,9 +75,12 @@ constexpr int kParts = 14;                    // split path: workgroups per toke
 constexpr int kPartThreads = kSegs / kParts;  // 64 = one wave
 constexpr int kSlot = 20;                     // floats per (token, part) workspace slot
 constexpr int kSlotYsq = kSlot - 1;           // where a part's sum of y^2 goes
-constexpr int kCounterStride = 16;            // uint64 words between token counters (128 B)
+constexpr int kCounterStride = ATTNRES_COUNTER_STRIDE_BYTES / 8;  // uint64 words between counters
 constexpr int kSpinLimit = 1 << 20;           // bounded cross-workgroup wait
-constexpr int kAutoSplitMaxTokens = 32;       // attnres_fwd uses the split path up to here
+// attnres_fwd takes the split path for a single token with at least this
+// many block rows; everywhere else one workgroup per token is faster (the
+// cross-workgroup exchange costs about 1 us per phase).
+constexpr int kAutoSplitMinBlocks = 6;
 constexpr float kInvHidden = 1.0f / kHidden;
 
 static_assert(kSegs * kSeg == kHidden, "hidden size must be a multiple of 8");
@@ -450,7 +459,7 @@ __device__ __forceinline__ void arrive_and_wait(unsigned long long *cnt, unsigne
       __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(ATTNRES_SPIN_SLEEP);
   }
 }
 
@@ -604,7 +613,7 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   if (a.T == 0) return ATTNRES_OK;
 
   bool split = path == ATTNRES_PATH_SPLIT ||
-               (path == ATTNRES_PATH_AUTO && a.T <= kAutoSplitMaxTokens);
+               (path == ATTNRES_PATH_AUTO && a.T == 1 && a.num_blocks >= kAutoSplitMinBlocks);
   if (split && a.T > ATTNRES_SPLIT_MAX_TOKENS) return ATTNRES_E_UNSUPPORTED;
 
   KParams kp{};
