@@ -193,6 +193,26 @@ def bench_decode(steps: int):
     return res
 
 
+def bench_long(steps: int = 20):
+    """Long prefill (T=8192 and 4096, padded bank, heavy-tailed rows, no delta,
+    no norm): reported as extra information, one resident set each (the 1.2 GB
+    and 0.6 GB footprints exceed the Infinity Cache)."""
+    res = {}
+    for T in (8192, 4096):
+        case = W.long_prefill(T)
+        s = Set(W.make_inputs(case))
+        s.call()
+        torch.cuda.synchronize()
+        t = time_graph([s.call], steps, replays=3)
+        us = pct([x / steps * 1e3 for x in t], 50)
+        res[f"T{T}"] = dict(us=round(us, 2), GBps=round(case.algorithmic_bytes() / us / 1e3, 1),
+                            frac=round(case.algorithmic_bytes() / us / 1e3 / HBM_PEAK_GBPS, 4))
+        log(f"long prefill T={T}: {us:.1f} us, {res[f'T{T}']['GBps']:.0f} GB/s")
+        del s
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_s: float = 10.0):
     """The fp64 oracle, as it stands, on the host: whole mid-prefill calls
     (T=1024, 8 block rows) repeated until about target_s of CPU work."""
@@ -345,6 +365,7 @@ def main():
 
     mid = None if args.only == "decode" else bench_mid(args.steps, args.warmup, args.eager)
     decode = None if (args.only == "mid" or args.eager) else bench_decode(args.steps)
+    longp = None if (args.only or args.eager) else bench_long()
     if A.attnres_device_status() != A.ATTNRES_OK:
         raise SystemExit("device wait flag raised during the benchmark")
     cpu = None if (args.no_cpu or args.only) else cpu_baseline()
@@ -375,6 +396,8 @@ def main():
         if mid is None:
             line.update({"value": round(decode["nb8"]["cold_us"], 3), "unit": "us/call",
                          "higher_is_better": False})
+    if longp is not None:
+        line["long_prefill"] = longp
     if cpu is not None:
         line["cpu_baseline"] = cpu
     line["kernel_source_hash"] = kernel_source_hash()

@@ -45,9 +45,6 @@
 #ifndef ATTNRES_ROW_WGS_PER_CU
 #define ATTNRES_ROW_WGS_PER_CU 0        // 0: one workgroup per token; k: k per CU, looping
 #endif
-#ifndef ATTNRES_COUNTER_STRIDE_BYTES
-#define ATTNRES_COUNTER_STRIDE_BYTES 128  // spacing of the split path's per-token counters
-#endif
 #ifndef ATTNRES_SPIN_SLEEP
 #define ATTNRES_SPIN_SLEEP 1              // s_sleep argument between polls (x64 cycles)
 #endif
@@ -56,6 +53,12 @@
 #endif
 #ifndef ATTNRES_NT_STORES
 #define ATTNRES_NT_STORES 1             // streaming rows written non-temporally
+#endif
+#ifndef ATTNRES_NT_STORE_CUR
+#define ATTNRES_NT_STORE_CUR ATTNRES_NT_STORES  // policy for the in-place prefix / bank rows
+#endif
+#ifndef ATTNRES_EARLY_CUR_STORE
+#define ATTNRES_EARLY_CUR_STORE 0       // write prefix / bank rows as soon as cur exists
 #endif
 
 namespace attnres {
@@ -73,14 +76,16 @@ constexpr int kRowThreads = kSegs / kRowSegsPerLane;  // 448 = 7 waves
 constexpr int kRowWaves = kRowThreads / kWave;        // 7
 constexpr int kParts = 14;                    // split path: workgroups per token
 constexpr int kPartThreads = kSegs / kParts;  // 64 = one wave
-constexpr int kSlot = 20;                     // floats per (token, part) workspace slot
+constexpr int kSlot = 20;                     // 64-bit words per (token, part) workspace slot
 constexpr int kSlotYsq = kSlot - 1;           // where a part's sum of y^2 goes
-constexpr int kCounterStride = ATTNRES_COUNTER_STRIDE_BYTES / 8;  // uint64 words between counters
 constexpr int kSpinLimit = 1 << 20;           // bounded cross-workgroup wait
-// attnres_fwd takes the split path for a single token with at least this
-// many block rows; everywhere else one workgroup per token is faster (the
-// cross-workgroup exchange costs about 1 us per phase).
+// attnres_fwd takes the split path for up to kAutoSplitMaxTokens tokens with
+// at least kAutoSplitMinBlocks block rows: there one CU per token would spend
+// longer loading and reducing the rows than the cross-workgroup exchange
+// (about 1 us per phase) costs.  Everywhere else one workgroup per token is
+// faster.
 constexpr int kAutoSplitMinBlocks = 6;
+constexpr int kAutoSplitMaxTokens = 8;
 constexpr float kInvHidden = 1.0f / kHidden;
 
 static_assert(kSegs * kSeg == kHidden, "hidden size must be a multiple of 8");
@@ -103,8 +108,7 @@ struct KParams {
   float out_eps;
   int widx;
   int T;
-  float *ws_part;
-  unsigned long long *ws_count;
+  uint64_t *ws_part;
   unsigned *ws_flag;
 };
 
@@ -124,12 +128,12 @@ __device__ __forceinline__ u32x4 load_stream(const uint16_t *p) {
 __device__ __forceinline__ u32x4 load_cached(const uint16_t *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
+template <bool NT = ATTNRES_NT_STORES>
 __device__ __forceinline__ void store_stream(uint16_t *p, u32x4 v) {
-#if ATTNRES_NT_STORES
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-#else
-  *reinterpret_cast<u32x4 *>(p) = v;
-#endif
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+  else
+    *reinterpret_cast<u32x4 *>(p) = v;
 }
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32.
@@ -297,8 +301,26 @@ struct Token {
     }
   }
 
-  // out = bf16_RNE(y * rsig * w) (or y), then the in-place writes of cur,
-  // after every read of this lane's elements.
+  // The in-place writes of cur (prefix with a delta, bank slot widx).  By the
+  // time cur exists every load of this lane has completed (the wait counter
+  // retires loads in issue order and prefix / delta were issued last), and a
+  // lane only rewrites elements it has already read, so the writes may be
+  // issued from then on.
+  __device__ __forceinline__ void store_cur(const KParams &p, int64_t t, int seg0,
+                                            int seg_step) const {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int64_t off = int64_t(seg0 + i * seg_step) * kSeg;
+      if constexpr (DELTA)
+        store_stream<ATTNRES_NT_STORE_CUR>(p.prefix + t * kHidden + off, x[NB][i]);
+      if (p.widx >= 0)
+        store_stream<ATTNRES_NT_STORE_CUR>(
+            p.blocks + t * p.tok_stride + p.widx * p.slot_stride + off, x[NB][i]);
+    }
+  }
+
+  // out = bf16_RNE(y * rsig * w) (or y), then (unless already done) the
+  // in-place writes of cur.
   __device__ __forceinline__ void store(const KParams &p, int64_t t, int seg0, int seg_step,
                                         const float (&y)[SPL][8], float rsig) const {
 #pragma unroll
@@ -314,10 +336,8 @@ struct Token {
           o[k] = pack_bf16x2(y[i][2 * k], y[i][2 * k + 1]);
       }
       store_stream(p.out + t * kHidden + off, o);
-      if constexpr (DELTA) store_stream(p.prefix + t * kHidden + off, x[NB][i]);
-      if (p.widx >= 0)
-        store_stream(p.blocks + t * p.tok_stride + p.widx * p.slot_stride + off, x[NB][i]);
     }
+    if (!ATTNRES_EARLY_CUR_STORE) store_cur(p, t, seg0, seg_step);
   }
 };
 
@@ -398,6 +418,7 @@ attnres_row_kernel(KParams p) {
     u32x4 qh[SPL], ql[SPL];
     tk.query(qh, ql);
     tk.finish_cur();
+    if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, threadIdx.x, kRowThreads);
 
     float ss[NS], dq[NS];
     tk.partials(qh, ql, ss, dq);
@@ -441,25 +462,53 @@ attnres_row_kernel(KParams p) {
 // split path: kParts single-wave workgroups per token
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float load_agent(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The exchange between the kParts workgroups of a token crosses XCDs, whose
+// L2 caches are not coherent with each other.  Every exchanged value is a
+// self-validating 64-bit word, (generation << 32) | float bits, written and
+// read with single device-coherent (agent-scope atomic) accesses, which bypass
+// the non-coherent L2: no L2 writeback or invalidate, no counter, and a reader
+// needs one round trip once the words are there.  A part's generation for this
+// call is its own word 0's generation plus one: every call rewrites word 0 of
+// all kParts parts of a token with the same generation, so the parts agree
+// without communicating (the workspace starts at zero).  Waits are bounded; a
+// wait that gives up raises the device flag.
+__device__ __forceinline__ uint64_t tagged_load(const uint64_t *w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void tagged_store(uint64_t *w, float v, uint32_t gen) {
+  __hip_atomic_store(w, (uint64_t(gen) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t tag_of(uint64_t w) { return uint32_t(w >> 32); }
+__device__ __forceinline__ float value_of(uint64_t w) { return __uint_as_float(uint32_t(w)); }
 
-// Arrive at the token's counter and wait until all kParts workgroups of this
-// phase have arrived.  The counter only grows: the k-th phase of a token
-// completes when it reaches k * kParts, so arrival value `old` belongs to the
-// phase ending at (old / kParts + 1) * kParts.  Called by one lane.
-__device__ __forceinline__ void arrive_and_wait(unsigned long long *cnt, unsigned *flag) {
-  const unsigned long long old =
-      __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long target = (old / kParts + 1) * kParts;
-  int spins = 0;
-  while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    if (++spins > kSpinLimit) {
+// Sums word i0 and word i1 over the kParts parts (fixed order), once every
+// part has written them with generation `gen`.
+__device__ __forceinline__ void gather2(const uint64_t *tok_ws, int i0, int i1, uint32_t gen,
+                                        unsigned *flag, float &s0, float &s1) {
+  uint64_t a[kParts], b[kParts];
+  for (int spins = 0;; ++spins) {
+    bool ready = true;
+#pragma unroll
+    for (int r = 0; r < kParts; ++r) {
+      a[r] = tagged_load(tok_ws + r * kSlot + i0);
+      b[r] = tagged_load(tok_ws + r * kSlot + i1);
+    }
+#pragma unroll
+    for (int r = 0; r < kParts; ++r) ready = ready && tag_of(a[r]) == gen && tag_of(b[r]) == gen;
+    if (ready) break;
+    if (spins >= kSpinLimit) {
       __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     __builtin_amdgcn_s_sleep(ATTNRES_SPIN_SLEEP);
+  }
+  s0 = 0.f;
+  s1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < kParts; ++r) {
+    s0 += value_of(a[r]);
+    s1 += value_of(b[r]);
   }
 }
 
@@ -469,12 +518,18 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   const int64_t t = blockIdx.x / kParts;
   const int part = blockIdx.x - int(t) * kParts;
   const int lane = threadIdx.x;
+  uint64_t *const tok_ws = p.ws_part + size_t(t) * kParts * kSlot;
+  uint64_t *const slot = tok_ws + part * kSlot;
+
+  // This call's generation (issued first; used only when publishing).
+  const uint32_t gen = tag_of(tagged_load(slot)) + 1u;
 
   Token<NB, DELTA, ONORM, 1> tk;
   tk.issue(p, t, part * kPartThreads + lane, 0);
   u32x4 qh[1], ql[1];
   tk.query(qh, ql);
   tk.finish_cur();
+  if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, part * kPartThreads + lane, 0);
 
   float ss[NS], dq[NS];
   tk.partials(qh, ql, ss, dq);
@@ -484,27 +539,18 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     ss[j] = wave_sum_lane63(ss[j]);
     dq[j] = wave_sum_lane63(dq[j]);
   }
-  float *const tok_ws = p.ws_part + size_t(t) * kParts * kSlot;
-  unsigned long long *const cnt = p.ws_count + size_t(t) * kCounterStride;
   if (lane == kWave - 1) {
-    float *const slot = tok_ws + part * kSlot;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      slot[j] = ss[j];
-      slot[NS + j] = dq[j];
+      tagged_store(slot + j, ss[j], gen);
+      tagged_store(slot + NS + j, dq[j], gen);
     }
-    arrive_and_wait(cnt, p.ws_flag);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   float logit = 0.f;
   if (lane < NS) {
-    float s = 0.f, d = 0.f;
-#pragma unroll
-    for (int r = 0; r < kParts; ++r) {
-      s += load_agent(tok_ws + r * kSlot + lane);
-      d += load_agent(tok_ws + r * kSlot + NS + lane);
-    }
+    float s, d;
+    gather2(tok_ws, lane, NS + lane, gen, p.ws_flag, s, d);
     logit = d * rsqrtf(s * kInvHidden + p.rms_eps);
   }
   const float p_lane = softmax_lanes<NS>(logit);
@@ -514,14 +560,9 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   float rsig = 1.f;
   if constexpr (ONORM) {
     const float sy = wave_sum_lane63(sum_sq<1>(y));
-    if (lane == kWave - 1) {
-      tok_ws[part * kSlot + kSlotYsq] = sy;
-      arrive_and_wait(cnt, p.ws_flag);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    float tot = 0.f;
-#pragma unroll
-    for (int r = 0; r < kParts; ++r) tot += load_agent(tok_ws + r * kSlot + kSlotYsq);
+    if (lane == kWave - 1) tagged_store(slot + kSlotYsq, sy, gen);
+    float tot, unused;
+    gather2(tok_ws, kSlotYsq, kSlotYsq, gen, p.ws_flag, tot, unused);
     rsig = rsqrtf(tot * kInvHidden + p.out_eps);
   }
   tk.store(p, t, part * kPartThreads + lane, 0, y, rsig);
@@ -560,15 +601,13 @@ KernelFn pick(bool split, int nb, bool d, bool o) {
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxDevices = 64;
-constexpr size_t kPartBytes = size_t(ATTNRES_SPLIT_MAX_TOKENS) * kParts * kSlot * sizeof(float);
-constexpr size_t kCountBytes = size_t(ATTNRES_SPLIT_MAX_TOKENS) * kCounterStride * 8;
+constexpr size_t kPartBytes = size_t(ATTNRES_SPLIT_MAX_TOKENS) * kParts * kSlot * sizeof(uint64_t);
 constexpr size_t kFlagBytes = 256;
-constexpr size_t kWorkspaceBytes = kPartBytes + kCountBytes + kFlagBytes;
+constexpr size_t kWorkspaceBytes = kPartBytes + kFlagBytes;
 
 struct DeviceWorkspace {
   void *base = nullptr;
-  float *part = nullptr;
-  unsigned long long *count = nullptr;
+  uint64_t *part = nullptr;
   unsigned *flag = nullptr;
 };
 
@@ -598,9 +637,8 @@ int init_device_locked(int device) {
   }
   DeviceWorkspace &w = g_ws[device];
   w.base = base;
-  w.part = static_cast<float *>(base);
-  w.count = reinterpret_cast<unsigned long long *>(static_cast<char *>(base) + kPartBytes);
-  w.flag = reinterpret_cast<unsigned *>(static_cast<char *>(base) + kPartBytes + kCountBytes);
+  w.part = static_cast<uint64_t *>(base);
+  w.flag = reinterpret_cast<unsigned *>(static_cast<char *>(base) + kPartBytes);
   (void)hipSetDevice(prev);
   return ATTNRES_OK;
 }
@@ -613,7 +651,8 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   if (a.T == 0) return ATTNRES_OK;
 
   bool split = path == ATTNRES_PATH_SPLIT ||
-               (path == ATTNRES_PATH_AUTO && a.T == 1 && a.num_blocks >= kAutoSplitMinBlocks);
+               (path == ATTNRES_PATH_AUTO && a.T <= kAutoSplitMaxTokens &&
+                a.num_blocks >= kAutoSplitMinBlocks);
   if (split && a.T > ATTNRES_SPLIT_MAX_TOKENS) return ATTNRES_E_UNSUPPORTED;
 
   KParams kp{};
@@ -647,7 +686,6 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
       if (rc != ATTNRES_OK) return rc;
     }
     kp.ws_part = g_ws[dev].part;
-    kp.ws_count = g_ws[dev].count;
     kp.ws_flag = g_ws[dev].flag;
   }
 
@@ -761,7 +799,8 @@ extern "C" int attnres_device_status(int device) {
   if (e == hipSuccess) e = hipMemcpy(&flag, w.flag, sizeof flag, hipMemcpyDeviceToHost);
   int rc = ATTNRES_OK;
   if (e == hipSuccess && flag != 0) {
-    // A wait gave up: phases may be out of step, so restart every counter.
+    // A wait gave up: parts of a token may disagree on the generation, so
+    // restart every word at generation zero.
     e = hipMemset(w.base, 0, kWorkspaceBytes);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     rc = ATTNRES_E_DEVICE_WAIT;

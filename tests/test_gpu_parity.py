@@ -139,24 +139,49 @@ def test_bitwise_repeatable(G):
         assert all((o == outs[0]).all() for o in outs), f"path {path} not repeatable"
 
 
-def test_split_counters_across_many_calls(G):
-    """The split path's arrival counters never reset: alternate one- and
-    two-phase calls (without / with output norm) many times and keep checking
-    results, then the device fault flag must be clear."""
+def test_split_exchange_across_many_calls(G):
+    """The split path's exchange words carry a generation that advances every
+    call and is never reset: run many consecutive calls, alternating one-phase
+    and two-phase calls (without / with output norm), different token counts
+    and block counts, and check every result; the device fault flag must stay
+    clear."""
     from kimi_k3_attention_amd import attnres as A
-    cases = [W.Case("ctr_a", T=5, nb=4, has_onorm=True, seed=60),
-             W.Case("ctr_b", T=7, nb=8, has_onorm=False, seed=61)]
+    cases = [W.Case("xa", T=5, nb=4, has_onorm=True, seed=60),
+             W.Case("xb", T=7, nb=8, has_onorm=False, seed=61),
+             W.Case("xc", T=1, nb=8, has_onorm=True, widx=7, seed=62),
+             W.Case("xd", T=64, nb=6, has_onorm=True, widx=0, seed=63)]
     prepared = []
     for c in cases:
         inp = W.make_inputs(c)
         prepared.append((inp, G.oracle_full(inp)))
-    for it in range(40):
-        inp, ref = prepared[it % 2]
+    for it in range(60):
+        inp, ref = prepared[it % len(prepared)]
         d = G.upload(inp)
         G.run(d, path=A.ATTNRES_PATH_SPLIT)
-        if it % 8 < 2:
-            G.check_full(inp, G.download(d), ref)
+        G.check_full(inp, G.download(d), ref)
+    assert A.attnres_device_status() == A.ATTNRES_OK
+
+
+def test_split_back_to_back_without_sync(G):
+    """Consecutive split calls on one stream with no host synchronisation in
+    between (each reuses the same workspace words), results checked after."""
+    from kimi_k3_attention_amd import attnres as A
+    cases = [W.Case(f"bb{k}", T=3, nb=7, widx=2, seed=70 + k) for k in range(8)]
+    inps = [W.make_inputs(c) for c in cases]
+    refs = [G.oracle_full(i) for i in inps]
+    devs = [G.upload(i) for i in inps]
     torch.cuda.synchronize()
+    for _ in range(3):
+        for dv in devs:
+            dv.out.fill_(0)
+        for k, dv in enumerate(devs):
+            # restore the in-place buffers so every call sees its original inputs
+            dv.prefix.copy_(G.to_dev(inps[k].prefix))
+            dv.bank.copy_(G.to_dev(inps[k].bank))
+        for dv in devs:
+            G.run(dv, path=A.ATTNRES_PATH_SPLIT)
+        for k, dv in enumerate(devs):
+            G.check_full(inps[k], G.download(dv), refs[k])
     assert A.attnres_device_status() == A.ATTNRES_OK
 
 
