@@ -59,7 +59,8 @@ extern "C" {
 #define ATTNRES_E_DEVICE_WAIT -13 /* a split-path cross-workgroup wait gave up (device flag) */
 
 /* ---- path selectors for attnres_fwd_path -------------------------------- */
-#define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: split for T <= 8 with >= 6 blocks, else row */
+#define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: split for T <= 16 (<= 32 with >= 2 blocks,
+                                <= 64 with >= 7 blocks), else row */
 #define ATTNRES_PATH_ROW 1   /* one workgroup per token */
 #define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (T <= 256) */
 

@@ -76,23 +76,23 @@ constexpr int kRowThreads = kSegs / kRowSegsPerLane;  // 448 = 7 waves
 constexpr int kRowWaves = kRowThreads / kWave;        // 7
 constexpr int kParts = 14;                    // split path: workgroups per token
 constexpr int kPartThreads = kSegs / kParts;  // 64 = one wave
-constexpr int kSlot = 20;                     // 64-bit words per (token, part) workspace slot
+constexpr int kSlot = 64;                     // 64-bit words per (token, part) workspace slot
 constexpr int kSlotYsq = kSlot - 1;           // where a part's sum of y^2 goes
 constexpr int kSpinLimit = 1 << 20;           // bounded cross-workgroup wait
-// attnres_fwd takes the split path for up to kAutoSplitMaxTokens tokens with
-// at least kAutoSplitMinBlocks block rows: there one CU per token would spend
-// longer loading and reducing the rows than the cross-workgroup exchange
-// (about 1 us per phase) costs.  Everywhere else one workgroup per token is
-// faster.
-constexpr int kAutoSplitMinBlocks = 6;
-constexpr int kAutoSplitMaxTokens = 8;
+// attnres_fwd's choice of kernel, from measured latency per call: spreading a
+// token over 14 CUs (split) beats one CU per token (row) while the grid is
+// small, the more so the more block rows a token has.
+__host__ __device__ constexpr bool auto_split(int64_t T, int nb) {
+  return T <= 16 || (T <= 32 && nb >= 2) || (T <= 64 && nb >= 7);
+}
 constexpr float kInvHidden = 1.0f / kHidden;
 
 static_assert(kSegs * kSeg == kHidden, "hidden size must be a multiple of 8");
 static_assert(kRowThreads % kWave == 0 && kRowThreads * kRowSegsPerLane == kSegs,
               "row workgroup must be whole waves covering the row");
 static_assert(kPartThreads == kWave, "a split part is one wave");
-static_assert(2 * (kMaxBlocks + 1) < kSlotYsq, "workspace slot too small");
+static_assert((kMaxBlocks + 1) * (kMaxBlocks + 2) / 2 + kMaxBlocks + 1 <= kSlotYsq,
+              "workspace slot too small");
 
 struct KParams {
   uint16_t *prefix;
@@ -482,20 +482,17 @@ __device__ __forceinline__ void tagged_store(uint64_t *w, float v, uint32_t gen)
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return uint32_t(w >> 32); }
 __device__ __forceinline__ float value_of(uint64_t w) { return __uint_as_float(uint32_t(w)); }
 
-// Sums word i0 and word i1 over the kParts parts (fixed order), once every
-// part has written them with generation `gen`.
-__device__ __forceinline__ void gather2(const uint64_t *tok_ws, int i0, int i1, uint32_t gen,
-                                        unsigned *flag, float &s0, float &s1) {
-  uint64_t a[kParts], b[kParts];
+// Sums word `idx` over the kParts parts (fixed order), once every part has
+// written it with generation `gen`.
+__device__ __forceinline__ float gather(const uint64_t *tok_ws, int idx, uint32_t gen,
+                                        unsigned *flag) {
+  uint64_t w[kParts];
   for (int spins = 0;; ++spins) {
     bool ready = true;
 #pragma unroll
-    for (int r = 0; r < kParts; ++r) {
-      a[r] = tagged_load(tok_ws + r * kSlot + i0);
-      b[r] = tagged_load(tok_ws + r * kSlot + i1);
-    }
+    for (int r = 0; r < kParts; ++r) w[r] = tagged_load(tok_ws + r * kSlot + idx);
 #pragma unroll
-    for (int r = 0; r < kParts; ++r) ready = ready && tag_of(a[r]) == gen && tag_of(b[r]) == gen;
+    for (int r = 0; r < kParts; ++r) ready = ready && tag_of(w[r]) == gen;
     if (ready) break;
     if (spins >= kSpinLimit) {
       __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -503,18 +500,47 @@ __device__ __forceinline__ void gather2(const uint64_t *tok_ws, int i0, int i1, 
     }
     __builtin_amdgcn_s_sleep(ATTNRES_SPIN_SLEEP);
   }
-  s0 = 0.f;
-  s1 = 0.f;
+  float s = 0.f;
 #pragma unroll
-  for (int r = 0; r < kParts; ++r) {
-    s0 += value_of(a[r]);
-    s1 += value_of(b[r]);
-  }
+  for (int r = 0; r < kParts; ++r) s += value_of(w[r]);
+  return s;
 }
+
+__device__ __forceinline__ float lane_shuffle(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+// Row j of the upper-triangular pair list (j <= k, row-major) starts here.
+__host__ __device__ constexpr int pair_row_start(int ns, int j) { return j * ns - j * (j - 1) / 2; }
+
+// The values one part publishes.  With an output norm: the Gram matrix of the
+// sources over this part's elements, G_jk = sum x_j x_k for j <= k (its
+// diagonal is the sum of squares), followed by the query dots; the output
+// norm's sum of squares then follows from ||y||^2 = sum_jk p_j p_k G_jk with
+// no second exchange.  Without one: the sums of squares, then the query dots.
+template <int NS, bool ONORM>
+struct SplitWords {
+  static constexpr int kPairs = NS * (NS + 1) / 2;
+  static constexpr int kCount = ONORM ? kPairs + NS : 2 * NS;
+  static constexpr int kDot = ONORM ? kPairs : NS;  // first query-dot word
+  __device__ static constexpr int ss_word(int j) { return ONORM ? pair_row_start(NS, j) : j; }
+};
+
+// ||y||^2 is taken from the Gram matrix only when it is not much smaller than
+// its triangle-inequality bound (sum_j p_j ||x_j||)^2; below this fraction the
+// sources cancel, the Gram form loses relative accuracy, and the sum of
+// squares of y is exchanged directly instead.
+constexpr float kGramGuard = 1.f / 16.f;
 
 template <int NB, bool DELTA, bool ONORM>
 __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) {
   constexpr int NS = NB + 1;
+  using Words = SplitWords<NS, ONORM>;
+  constexpr int NV = Words::kCount;
+  constexpr int kTrStride = kWave + 4;  // padded: conflict-free 128-bit reads
+  static_assert(NV <= kSlotYsq, "workspace slot too small");
+  __shared__ __align__(16) float s_tr[NV][kTrStride];
+
   const int64_t t = blockIdx.x / kParts;
   const int part = blockIdx.x - int(t) * kParts;
   const int lane = threadIdx.x;
@@ -531,38 +557,80 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   tk.finish_cur();
   if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, part * kPartThreads + lane, 0);
 
-  float ss[NS], dq[NS];
-  tk.partials(qh, ql, ss, dq);
-  tk.keep_packed();
+  // Per-lane values, transposed through LDS so that lane v sums value v over
+  // the wave, then published with one store of tagged words.
+  {
+    float ss[NS], dq[NS];
+    tk.partials(qh, ql, ss, dq);
+    if constexpr (ONORM) {
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    ss[j] = wave_sum_lane63(ss[j]);
-    dq[j] = wave_sum_lane63(dq[j]);
-  }
-  if (lane == kWave - 1) {
+      for (int j = 0; j < NS; ++j) {
+        s_tr[pair_row_start(NS, j)][lane] = ss[j];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      tagged_store(slot + j, ss[j], gen);
-      tagged_store(slot + NS + j, dq[j], gen);
+        for (int k = j + 1; k < NS; ++k) {
+          float g = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) g = dot2(tk.x[j][0][w], tk.x[k][0][w], g);
+          s_tr[pair_row_start(NS, j) + (k - j)][lane] = g;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) s_tr[j][lane] = ss[j];
     }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) s_tr[Words::kDot + j][lane] = dq[j];
+  }
+  tk.keep_packed();
+  __syncthreads();
+  if (lane < NV) {
+    const float4 *row = reinterpret_cast<const float4 *>(s_tr[lane]);
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWave / 4; ++i) {
+      const float4 a = row[i];
+      v += a.x;
+      v += a.y;
+      v += a.z;
+      v += a.w;
+    }
+    tagged_store(slot + lane, v, gen);
   }
 
-  float logit = 0.f;
-  if (lane < NS) {
-    float s, d;
-    gather2(tok_ws, lane, NS + lane, gen, p.ws_flag, s, d);
-    logit = d * rsqrtf(s * kInvHidden + p.rms_eps);
-  }
+  // The token's totals: lane v holds word v summed over the parts.
+  const float total = lane < NV ? gather(tok_ws, lane, gen, p.ws_flag) : 0.f;
+  const int jl = lane < NS ? lane : 0;
+  const float ss_j = lane_shuffle(total, Words::ss_word(jl));
+  const float dq_j = lane_shuffle(total, Words::kDot + jl);
+  const float logit = lane < NS ? dq_j * rsqrtf(ss_j * kInvHidden + p.rms_eps) : 0.f;
   const float p_lane = softmax_lanes<NS>(logit);
   float y[1][8];
   tk.mix(p_lane, y);
 
   float rsig = 1.f;
   if constexpr (ONORM) {
-    const float sy = wave_sum_lane63(sum_sq<1>(y));
-    if (lane == kWave - 1) tagged_store(slot + kSlotYsq, sy, gen);
-    float tot, unused;
-    gather2(tok_ws, kSlotYsq, kSlotYsq, gen, p.ws_flag, tot, unused);
+    // Lane w < kPairs holds G_jk for the w-th pair (j <= k).
+    int j = 0, rem = lane;
+#pragma unroll
+    for (int r = 0; r < NS; ++r)
+      if (rem >= NS - j && j < NS - 1) {
+        rem -= NS - j;
+        ++j;
+      }
+    const int k = j + rem;
+    const float pj = lane_shuffle(p_lane, j);
+    const float pk = lane_shuffle(p_lane, k < NS ? k : 0);
+    const float term = lane < Words::kPairs ? (j == k ? 1.f : 2.f) * pj * pk * total : 0.f;
+    const float bound = lane < NS ? p_lane * sqrtf(fmaxf(ss_j, 0.f)) : 0.f;
+    const float ysq = lane_value(wave_sum_lane63(term), kWave - 1);
+    const float b = lane_value(wave_sum_lane63(bound), kWave - 1);
+    float tot = ysq;
+    if (!(ysq >= kGramGuard * b * b)) {
+      // Every part sees the same totals and takes the same branch.
+      const float sy = wave_sum_lane63(sum_sq<1>(y));
+      if (lane == kWave - 1) tagged_store(slot + kSlotYsq, sy, gen);
+      tot = gather(tok_ws, kSlotYsq, gen, p.ws_flag);
+    }
     rsig = rsqrtf(tot * kInvHidden + p.out_eps);
   }
   tk.store(p, t, part * kPartThreads + lane, 0, y, rsig);
@@ -651,8 +719,7 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   if (a.T == 0) return ATTNRES_OK;
 
   bool split = path == ATTNRES_PATH_SPLIT ||
-               (path == ATTNRES_PATH_AUTO && a.T <= kAutoSplitMaxTokens &&
-                a.num_blocks >= kAutoSplitMinBlocks);
+               (path == ATTNRES_PATH_AUTO && auto_split(a.T, a.num_blocks));
   if (split && a.T > ATTNRES_SPLIT_MAX_TOKENS) return ATTNRES_E_UNSUPPORTED;
 
   KParams kp{};

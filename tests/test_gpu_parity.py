@@ -139,6 +139,30 @@ def test_bitwise_repeatable(G):
         assert all((o == outs[0]).all() for o in outs), f"path {path} not repeatable"
 
 
+def test_cancelling_sources(G):
+    """Sources that cancel: a zero projection weight makes every weight 1/3,
+    slot 1 is the negation of slot 0 and the current residual is small, so
+    ||y|| is far below sum_j p_j ||x_j||.  The split path must notice that the
+    Gram form of ||y||^2 would lose accuracy and exchange it directly."""
+    case = W.Case("cancel_T4_nb2", T=4, nb=2, cap=2, widx=-1, seed=90)
+    inp = W.make_inputs(case)
+    inp.res_w[:] = 0
+    H, ts = case.H, case.token_stride
+    for t in range(case.T):
+        inp.bank[t * ts + H: t * ts + 2 * H] = inp.bank[t * ts: t * ts + H] ^ np.uint16(0x8000)
+    small = (G.widen(inp.prefix) * 0.01).astype(np.float32)
+    inp.prefix[:] = torch.from_numpy(small).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ref = G.oracle_full(inp)
+    y_norm = np.linalg.norm(ref.out_f64, axis=1)
+    assert np.all(ref.probs == ref.probs[:, :1])  # uniform weights
+    for path in _paths(case.T):
+        G.say(case.name, "path", path)
+        d = G.upload(inp)
+        G.run(d, path=path)
+        G.check_full(inp, G.download(d), ref)
+    assert np.isfinite(y_norm).all()
+
+
 def test_split_exchange_across_many_calls(G):
     """The split path's exchange words carry a generation that advances every
     call and is never reset: run many consecutive calls, alternating one-phase
