@@ -15,9 +15,18 @@ def pytest_configure(config):
         "markers", "slow: CPU test that takes more than a few seconds")
 
 
+@pytest.fixture(scope="session", autouse=True)
+def built_libraries():
+    """Builds libattnres and the oracle only if they are missing (a stale
+    build is the caller's to refresh: build() always recompiles)."""
+    from kimi_k3_attention_amd import build as kbuild
+    from oracle import build as obuild
+    if not os.path.exists(kbuild.LIB):
+        kbuild.build()
+    obuild.ensure_built()
+
+
 @pytest.fixture(scope="session")
-def oracle_lib():
-    from oracle import build
-    build.ensure_built()
+def oracle_lib(built_libraries):
     from oracle import oracle as o
     return o.load_library()
