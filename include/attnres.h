@@ -123,8 +123,8 @@ int attnres_validate(const void *prefix, const void *delta, const void *blocks,
                      const void *output_norm_weight, float output_norm_eps,
                      int block_write_idx, const void *out, int64_t T, int64_t H);
 
-/* Allocates and clears the split path's workspace on `device` (a few hundred
- * KB: cross-workgroup counters, partial sums and a fault flag).  Idempotent.
+/* Allocates and clears the split path's workspace on `device` (about 1.8 MB:
+ * tagged partial-sum words and a fault flag).  Idempotent.
  * Call it outside stream capture. */
 int attnres_init(int device);
 

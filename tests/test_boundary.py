@@ -23,7 +23,7 @@ def _declared_functions():
 def _declared_constants():
     text = open(HEADER).read()
     return {m.group(1): int(m.group(2))
-            for m in re.finditer(r"#define\s+(ATTNRES_[A-Z_]+)\s+(-?\d+)", text)}
+            for m in re.finditer(r"#define\s+(ATTNRES_[A-Z0-9_]+)\s+(-?\d+)", text)}
 
 
 @pytest.fixture(scope="module")

@@ -31,6 +31,11 @@ def _paths(T):
     return ps
 
 
+def _path_of(name):
+    from kimi_k3_attention_amd import attnres as A
+    return {"row": A.ATTNRES_PATH_ROW, "split": A.ATTNRES_PATH_SPLIT}[name]
+
+
 def _run_and_check_all_paths(G, case, ref=None):
     inp = W.make_inputs(case)
     if ref is None:
@@ -163,12 +168,48 @@ def test_cancelling_sources(G):
     assert np.isfinite(y_norm).all()
 
 
+@pytest.mark.parametrize("path_name", ["row", "split"])
+def test_bank_offsets_beyond_32_bits(G, path_name):
+    """A bank whose element offsets exceed 2^31 (token stride 2^24 elements,
+    about 4.8 GB): only the used rows are filled; sampled tokens are checked
+    against the oracle and the elements right after each written row keep
+    their sentinel."""
+    from kimi_k3_attention_amd import attnres as A
+    path = _path_of(path_name)
+    T, nb, cap, H, ts = 150, 5, 8, 7168, 1 << 24
+    case = W.Case("small_rows", T=T, nb=nb, cap=cap, widx=6, seed=95)
+    inp = W.make_inputs(case)                      # dense bank, used for the values
+    bank = torch.full((T * ts,), 0x7F81, dtype=torch.int16, device="cuda")
+    bank3 = bank.as_strided((T, cap, H), (ts, H, 1))
+    dense = G.to_dev(inp.bank).view(T, cap, H)
+    bank3.copy_(dense)
+    assert (T - 1) * ts + cap * H > 2 ** 31
+    d = G.upload(inp)
+    G.say(case.name, "path", path_name)
+    A.attnres_fwd(d.prefix, d.delta, bank3, nb, d.res_w, d.rms_w, case.eps, d.onw, case.oeps,
+                  case.widx, d.out, path=path)
+    torch.cuda.synchronize()
+    tokens = [0, 1, 74, T - 2, T - 1]
+    ref = G.oracle_sample(inp, tokens)
+    out = G.from_dev(d.out)
+    G.assert_out_close(out[tokens], ref.out_bits, "large-offset out")
+    assert (G.from_dev(d.prefix)[tokens] == ref.prefix_after).all()
+    written = G.from_dev(bank3[tokens, case.widx].contiguous())
+    assert (written == ref.written_row).all()
+    tail = G.from_dev(bank3[:, cap - 1, :].contiguous())    # slot 7: never read or written
+    assert (tail == inp.bank.reshape(T, cap, H)[:, cap - 1]).all()
+    after = bank.as_strided((T, 64), (ts, 1), storage_offset=cap * H)
+    assert (G.from_dev(after.contiguous()) == 0x7F81).all(), "write past a row"
+    del bank, bank3
+    torch.cuda.empty_cache()
+
+
 def test_split_exchange_across_many_calls(G):
     """The split path's exchange words carry a generation that advances every
-    call and is never reset: run many consecutive calls, alternating one-phase
-    and two-phase calls (without / with output norm), different token counts
-    and block counts, and check every result; the device fault flag must stay
-    clear."""
+    call and is never reset: run many consecutive calls, alternating calls
+    without and with output norm (one or two exchange phases), different
+    token counts and block counts, and check every result; the device fault
+    flag must stay clear."""
     from kimi_k3_attention_amd import attnres as A
     cases = [W.Case("xa", T=5, nb=4, has_onorm=True, seed=60),
              W.Case("xb", T=7, nb=8, has_onorm=False, seed=61),
@@ -216,7 +257,7 @@ def test_graph_replay_matches_eager(G, path_name):
     result every time.  delta = 0 makes repeated in-place calls a fixed point
     after the first."""
     from kimi_k3_attention_amd import attnres as A
-    path = A.ATTNRES_PATH_ROW if path_name == "row" else A.ATTNRES_PATH_SPLIT
+    path = _path_of(path_name)
     A.attnres_init()
     case = W.Case(f"graph_{path_name}", T=24, nb=6, widx=5, seed=70)
     inp = W.make_inputs(case)
