@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -78,12 +79,12 @@ class Set:
         if self.delta is not None:
             self.delta.zero_()  # repeated in-place calls stay a fixed point
 
-    def call(self, nb=None, token=None):
+    def call(self, nb=None, token=None, path=None):
         c = self.case
         nb = c.nb if nb is None else nb
         if token is None:
             A.attnres_fwd(self.prefix, self.delta, self.bank3, nb, self.res_w, self.rms_w, c.eps,
-                          self.onw, c.oeps, c.widx, self.out)
+                          self.onw, c.oeps, c.widx, self.out, path=path)
         else:
             sl = slice(token, token + 1)
             A.attnres_fwd(self.prefix[sl], None if self.delta is None else self.delta[sl],
@@ -213,28 +214,101 @@ def bench_long(steps: int = 20):
     return res
 
 
-def cpu_baseline(target_s: float = 10.0):
-    """The fp64 oracle, as it stands, on the host: whole mid-prefill calls
-    (T=1024, 8 block rows) repeated until about target_s of CPU work."""
+def _host_threads() -> int:
+    """Host threads for the multi-threaded oracle leg: the CPUs this process
+    may run on, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+HIDDEN_SWEEP = (2048, 2880, 4096, 5120, 7168, 8192, 12288, 16384)
+
+
+def bench_hidden_sweep(Hs=HIDDEN_SWEEP, T: int = 1024, steps: int = 120):
+    """The mid-prefill recipe (T=1024, 8 block rows, delta, output norm,
+    block_write_idx=3) at other hidden sizes, run by the any-H row kernel
+    (and, at 7168, also by the tuned row kernel): per-call time from graph
+    replay over enough resident input sets to exceed the Infinity Cache."""
+    res = {}
+    for H in Hs:
+        case = W.Case(f"hidden{H}_T{T}_nb8", T=T, nb=8, H=H, widx=3, seed=2)
+        footprint = 2 * T * H * (case.cap + 3)
+        nsets = max(1, -(-2 * MALL_BYTES // footprint))
+        sets = [Set(W.make_inputs(W.with_(case, seed=case.seed + 100 * r))) for r in range(nsets)]
+        nbytes = case.algorithmic_bytes()
+        paths = {"any_h": A.ATTNRES_PATH_ANY_H}
+        if H == 7168:
+            paths["tuned_row"] = A.ATTNRES_PATH_ROW
+        entry = {"bytes_per_call": nbytes, "input_sets": nsets}
+        for name, path in paths.items():
+            calls = [lambda st=st, path=path: st.call(path=path) for st in sets]
+            for fn in calls:
+                fn()
+            torch.cuda.synchronize()
+            t = time_graph(calls, steps, replays=3)
+            us = pct([x / steps * 1e3 for x in t], 50)
+            gbps = nbytes / us / 1e3
+            entry[name] = dict(us=round(us, 2), GBps=round(gbps, 1),
+                               frac=round(gbps / HBM_PEAK_GBPS, 4))
+            log(f"hidden sweep H={H} {name}: {us:.2f} us, {gbps:.0f} GB/s")
+        res[str(H)] = entry
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(single_s: float = 8.0, multi_s: float = 1.5):
+    """The fp64 oracle, as it stands, on the host, on whole mid-prefill calls
+    (T=1024, 8 block rows): single-threaded for about single_s, then with the
+    call's tokens split into contiguous ranges run by a pool of threads (the
+    C oracle runs without the GIL) for about multi_s of wall time."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     case = W.mid_prefill()
     inp = W.make_inputs(case)
-    args = (inp.prefix, inp.delta, inp.bank, case.token_stride, case.slot_stride, case.cap, case.nb,
-            inp.res_w, inp.rms_w, case.eps, inp.onw, case.oeps, case.widx)
-    oracle.attnres_oracle(*args)  # load / build
+    ts = case.token_stride
+
+    def run(a, b):
+        oracle.attnres_oracle(inp.prefix[a:b], None if inp.delta is None else inp.delta[a:b],
+                              inp.bank[a * ts:b * ts], ts, case.slot_stride, case.cap, case.nb,
+                              inp.res_w, inp.rms_w, case.eps, inp.onw, case.oeps, case.widx)
+
+    run(0, case.T)  # load / build
     t0 = time.perf_counter()
     calls = 0
     while True:
-        oracle.attnres_oracle(*args)
+        run(0, case.T)
         calls += 1
-        if time.perf_counter() - t0 >= target_s:
+        if time.perf_counter() - t0 >= single_s:
             break
-    dt = (time.perf_counter() - t0) / calls
-    gbps = case.algorithmic_bytes() / dt / 1e9
-    log(f"cpu oracle: {dt * 1e3:.0f} ms/call, {gbps:.3f} GB/s")
-    return dict(value=round(gbps, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{calls} whole calls of the T=1024 nb=8 workload (single-threaded C, fp64), "
-                       f"{dt * 1e3:.0f} ms/call")
+    dt1 = (time.perf_counter() - t0) / calls
+    gbps1 = case.algorithmic_bytes() / dt1 / 1e9
+    log(f"cpu oracle, 1 thread: {dt1 * 1e3:.0f} ms/call, {gbps1:.3f} GB/s")
+
+    n = _host_threads()
+    bounds = [(case.T * k // n, case.T * (k + 1) // n) for k in range(n)]
+    with ThreadPoolExecutor(max_workers=n) as pool:
+        list(pool.map(lambda ab: run(*ab), bounds))
+        t0 = time.perf_counter()
+        mcalls = 0
+        while True:
+            list(pool.map(lambda ab: run(*ab), bounds))
+            mcalls += 1
+            if time.perf_counter() - t0 >= multi_s:
+                break
+        dtn = (time.perf_counter() - t0) / mcalls
+    gbpsn = case.algorithmic_bytes() / dtn / 1e9
+    log(f"cpu oracle, {n} threads: {dtn * 1e3:.0f} ms/call, {gbpsn:.3f} GB/s")
+    return dict(value=round(gbpsn, 4), unit="GB/s", cores=n, kind="oracle",
+                sample=f"{mcalls} whole calls of the T=1024 nb=8 workload, tokens split over {n} "
+                       f"threads (C, fp64), {dtn * 1e3:.0f} ms/call; single-threaded: {calls} "
+                       f"calls, {dt1 * 1e3:.0f} ms/call",
+                single_thread=dict(value=round(gbps1, 4), unit="GB/s", cores=1,
+                                   ms_per_call=round(dt1 * 1e3, 1)),
+                ms_per_call=round(dtn * 1e3, 1))
 
 
 def load_traffic():
@@ -271,7 +345,9 @@ def _col(row, *names):
 
 
 def write_kernel_stats(trace_dir, out_name, title, command):
-    """profiles/<out_name>: the kernel-trace statistics of one profiling run."""
+    """profiles/<out_name>: the kernel-trace statistics of one profiling run,
+    then the libattnres dispatches grouped by kernel and workgroup size (one
+    group per launch shape, e.g. per hidden size of the any-H kernel)."""
     os.makedirs(PROFILES, exist_ok=True)
     lines = [f"# rocprofv3 kernel statistics, {title}", f"# command: {command}",
              f"# kernel source hash: {kernel_source_hash()}",
@@ -281,6 +357,24 @@ def write_kernel_stats(trace_dir, out_name, title, command):
                                  f"{float(_col(r, 'AverageNs')) / 1e3:.3f}",
                                  f"{float(_col(r, 'MinNs')) / 1e3:.3f}", f"{float(_col(r, 'MaxNs')) / 1e3:.3f}",
                                  f"{float(_col(r, 'Percentage')):.2f}"]))
+    groups = {}
+    for r in _csv_rows(trace_dir, "kernel_trace.csv"):
+        name = _col(r, "Kernel_Name")
+        if "attnres" not in name:
+            continue
+        m = re.search(r"(attnres_\w+_kernel<[^>]*>)", name)
+        short = m.group(1) if m else name[:60]
+        key = (short, int(_col(r, "Workgroup_Size_X")), int(_col(r, "Grid_Size_X")),
+               int(_col(r, "Scratch_Size")))
+        groups.setdefault(key, []).append(
+            (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3)
+    if groups:
+        lines += ["#", "# libattnres dispatches by launch shape (from the per-dispatch trace)",
+                  "# kernel | workgroup size | grid size (lanes) | scratch B/lane | "
+                  "dispatches | average us | median us"]
+        for (short, wg, grid, scr), ds in sorted(groups.items()):
+            lines.append(" | ".join([short, str(wg), str(grid), str(scr), str(len(ds)),
+                                     f"{float(np.mean(ds)):.3f}", f"{float(np.median(ds)):.3f}"]))
     with open(os.path.join(PROFILES, out_name), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -336,6 +430,8 @@ def main():
     ap.add_argument("--only", choices=["mid", "decode"], default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--calibrate", action="store_true", help="run the known-size copy for counters")
+    ap.add_argument("--hidden-sweep", action="store_true",
+                    help="only the T=1024 mid-prefill recipe at other hidden sizes (any-H kernel)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output directories")
     ap.add_argument("--profile-commands", default=None, help="JSON of the commands that made them")
@@ -362,6 +458,16 @@ def main():
     A.attnres_init()
     if args.calibrate:
         calibration_copy()
+    if args.hidden_sweep:
+        sweep = bench_hidden_sweep()
+        print(json.dumps({"metric": "attention-residual forward throughput at other hidden sizes",
+                          "unit": "GB/s", "higher_is_better": True, "data": "synthetic",
+                          "config": {"workload": "T=1024 tokens, 8 block rows, delta and output "
+                                                 "norm on, block_write_idx=3, bf16, dense bank",
+                                     "timing": "hipGraph replay"},
+                          "hidden_sizes": sweep, "kernel_source_hash": kernel_source_hash()}),
+              flush=True)
+        return
 
     mid = None if args.only == "decode" else bench_mid(args.steps, args.warmup, args.eager)
     decode = None if (args.only == "mid" or args.eager) else bench_decode(args.steps)

@@ -23,7 +23,11 @@
  * All reads see the state before the call (a written slot that is also a
  * source contributes its old value).  Bank slots num_blocks..max_blocks-1 are
  * never read, and nothing but out, prefix (with a delta) and the one bank row
- * per token is ever written.
+ * per token is ever written; with strided rows, the elements between rows are
+ * neither read nor written.
+ *
+ * Hidden size: any H that is a multiple of 8, up to ATTNRES_MAX_HIDDEN.  H =
+ * 7168 (Kimi-K3) runs on tuned kernels; other sizes on one any-H row kernel.
  *
  * Tensors are bf16 (passed as raw 16-bit patterns) in device memory.  The
  * library keeps no pointer after a call returns; the caller owns every buffer
@@ -46,11 +50,12 @@ extern "C" {
 #define ATTNRES_OK 0
 #define ATTNRES_E_NULL -1        /* a required pointer is NULL */
 #define ATTNRES_E_SHAPE -2       /* T < 0, H <= 0, max_blocks < 0, or sizes too large */
-#define ATTNRES_E_UNSUPPORTED -3 /* H != 7168, or a forced path that cannot run these sizes */
+#define ATTNRES_E_UNSUPPORTED -3 /* H not a multiple of 8 or > ATTNRES_MAX_HIDDEN, or a forced
+                                    path that cannot run these sizes */
 #define ATTNRES_E_NUM_BLOCKS -4  /* num_blocks < 0, > 8 or > max_blocks */
 #define ATTNRES_E_WRITE_IDX -5   /* block_write_idx < -1 or >= max_blocks */
-#define ATTNRES_E_ALIGN -6       /* a pointer not 16-byte aligned, or a bank stride not a multiple of 8 */
-#define ATTNRES_E_STRIDE -7      /* negative bank strides, or bank rows that overlap */
+#define ATTNRES_E_ALIGN -6       /* a pointer not 16-byte aligned, or a stride not a multiple of 8 */
+#define ATTNRES_E_STRIDE -7      /* a negative stride, or rows of one argument that overlap */
 #define ATTNRES_E_ALIAS -8       /* a written buffer overlaps another argument */
 #define ATTNRES_E_EPS -9         /* an epsilon that is negative or not finite */
 #define ATTNRES_E_NOT_INIT -10   /* the split path needs attnres_init() first (stream is capturing) */
@@ -59,13 +64,16 @@ extern "C" {
 #define ATTNRES_E_DEVICE_WAIT -13 /* a split-path cross-workgroup wait gave up (device flag) */
 
 /* ---- path selectors for attnres_fwd_path -------------------------------- */
-#define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: split for T <= 16 (<= 32 with >= 2 blocks,
-                                <= 64 with >= 7 blocks), else row */
-#define ATTNRES_PATH_ROW 1   /* one workgroup per token */
-#define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (T <= 256) */
+#define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: at H = 7168 split for T <= 16 (<= 32 with
+                                >= 2 blocks, <= 64 with >= 7 blocks), else row; other H: any-H */
+#define ATTNRES_PATH_ROW 1   /* one workgroup per token (the any-H kernel when H != 7168) */
+#define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (H = 7168, T <= 256) */
+#define ATTNRES_PATH_ANY_H 3 /* the any-H row kernel, also at H = 7168 */
 
 /* Largest T the split path accepts (its per-device workspace). */
 #define ATTNRES_SPLIT_MAX_TOKENS 256
+/* Largest hidden size (a multiple of 8). */
+#define ATTNRES_MAX_HIDDEN 16384
 
 /*
  * attnres_fwd -- the forward above, enqueued on `stream`.
@@ -87,7 +95,8 @@ extern "C" {
  *   output_norm_eps    >= 0, finite (ignored without an output norm).
  *   block_write_idx    -1 = no bank write, else 0..max_blocks-1.
  *   out      [T, H] bf16, row stride H, device; must not overlap any input.
- *   T, H     tokens (>= 0; T == 0 is a no-op) and hidden size (7168).
+ *   T, H     tokens (>= 0; T == 0 is a no-op) and hidden size (a multiple of
+ *            8, at most ATTNRES_MAX_HIDDEN).
  *   stream   a hipStream_t (NULL = the default stream).
  *
  * All device pointers must be 16-byte aligned.  Asynchronous: returns after
@@ -104,7 +113,7 @@ int attnres_fwd(void *prefix, const void *delta, void *blocks,
                 int block_write_idx, void *out, int64_t T, int64_t H,
                 void *stream);
 
-/* attnres_fwd with an explicit path (ATTNRES_PATH_*); both paths compute the
+/* attnres_fwd with an explicit path (ATTNRES_PATH_*); all paths compute the
  * same result within the fp32 rounding of their reduction orders. */
 int attnres_fwd_path(void *prefix, const void *delta, void *blocks,
                      int64_t block_token_stride, int64_t block_slot_stride,
@@ -114,6 +123,28 @@ int attnres_fwd_path(void *prefix, const void *delta, void *blocks,
                      int block_write_idx, void *out, int64_t T, int64_t H,
                      void *stream, int path);
 
+/*
+ * attnres_fwd_path with row strides for prefix, delta and out (in elements),
+ * e.g. views into wider activation buffers.  The reference dispatch gate (prhub
+ * digest of vLLM PR #54261, the attn_res.py snippet under "Key source
+ * snippets") sends hidden sizes other than 7168 and non-dense rows to a Triton
+ * fallback, and the code review on the vllm-ascend PR #14840 page asks for
+ * masked accesses when H is not a power of two; here both run natively.  Each stride must be >= H and a
+ * multiple of 8 when T > 1 (it is ignored when T <= 1); the elements between
+ * rows are never touched.  A written buffer must not share any element with
+ * another argument: row sets with equal strides are checked exactly (so
+ * interleaved rows of one wider buffer are accepted), other combinations by
+ * the address spans they cover.
+ */
+int attnres_fwd_strided(void *prefix, int64_t prefix_stride,
+                        const void *delta, int64_t delta_stride, void *blocks,
+                        int64_t block_token_stride, int64_t block_slot_stride,
+                        int max_blocks, int num_blocks,
+                        const void *res_w, const void *rms_w, float rms_eps,
+                        const void *output_norm_weight, float output_norm_eps,
+                        int block_write_idx, void *out, int64_t out_stride,
+                        int64_t T, int64_t H, void *stream, int path);
+
 /* The host-side argument checks of attnres_fwd, alone.  Makes no HIP call and
  * dereferences no pointer, so it runs without a GPU. */
 int attnres_validate(const void *prefix, const void *delta, const void *blocks,
@@ -122,6 +153,16 @@ int attnres_validate(const void *prefix, const void *delta, const void *blocks,
                      const void *res_w, const void *rms_w, float rms_eps,
                      const void *output_norm_weight, float output_norm_eps,
                      int block_write_idx, const void *out, int64_t T, int64_t H);
+
+/* The host-side argument checks of attnres_fwd_strided, alone (no HIP call). */
+int attnres_validate_strided(const void *prefix, int64_t prefix_stride,
+                             const void *delta, int64_t delta_stride, const void *blocks,
+                             int64_t block_token_stride, int64_t block_slot_stride,
+                             int max_blocks, int num_blocks,
+                             const void *res_w, const void *rms_w, float rms_eps,
+                             const void *output_norm_weight, float output_norm_eps,
+                             int block_write_idx, const void *out, int64_t out_stride,
+                             int64_t T, int64_t H);
 
 /* Allocates and clears the split path's workspace on `device` (about 1.8 MB:
  * tagged partial-sum words and a fault flag).  Idempotent.

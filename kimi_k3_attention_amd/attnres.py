@@ -23,7 +23,9 @@ ATTNRES_OK = 0
 ATTNRES_PATH_AUTO = 0
 ATTNRES_PATH_ROW = 1
 ATTNRES_PATH_SPLIT = 2
+ATTNRES_PATH_ANY_H = 3
 ATTNRES_SPLIT_MAX_TOKENS = 256
+ATTNRES_MAX_HIDDEN = 16384
 
 STATUS = {
     0: "ATTNRES_OK", -1: "ATTNRES_E_NULL", -2: "ATTNRES_E_SHAPE", -3: "ATTNRES_E_UNSUPPORTED",
@@ -52,6 +54,14 @@ _lib.attnres_fwd_path.argtypes = _FWD_ARGS + [_vp, _int]
 _lib.attnres_fwd_path.restype = _int
 _lib.attnres_validate.argtypes = list(_FWD_ARGS)
 _lib.attnres_validate.restype = _int
+# prefix, prefix_stride, delta, delta_stride, blocks, ts, ss, cap, nb, res_w, rms_w, eps,
+# onw, oeps, widx, out, out_stride, T, H
+_STRIDED_ARGS = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _int, _int, _vp, _vp, _f32, _vp, _f32,
+                 _int, _vp, _i64, _i64, _i64]
+_lib.attnres_fwd_strided.argtypes = _STRIDED_ARGS + [_vp, _int]
+_lib.attnres_fwd_strided.restype = _int
+_lib.attnres_validate_strided.argtypes = list(_STRIDED_ARGS)
+_lib.attnres_validate_strided.restype = _int
 _lib.attnres_init.argtypes = [_int]
 _lib.attnres_init.restype = _int
 _lib.attnres_shutdown.argtypes = []
@@ -86,17 +96,20 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _rows(name: str, t: Optional[torch.Tensor], T: int, H: int, required: bool):
+def _rows(name: str, t: Optional[torch.Tensor], T: int, H: int, required: bool) -> int:
+    """Checks a [T, H] matrix argument; returns its row stride in elements
+    (H when T <= 1, where the library ignores it)."""
     if t is None:
         if required:
             raise ValueError(f"{name} is required")
-        return
+        return H
     if t.dtype not in _BF16_LIKE:
         raise TypeError(f"{name} must be bf16 (got {t.dtype})")
     if t.dim() != 2 or t.shape[0] != T or t.shape[1] != H:
-        raise ValueError(f"{name} must be [{T}, {H}] with row stride {H}")
-    if T > 0 and (t.stride(1) != 1 or (T > 1 and t.stride(0) != H)):
-        raise ValueError(f"{name} must be [{T}, {H}] with row stride {H}")
+        raise ValueError(f"{name} must be [{T}, {H}] with unit element stride")
+    if T > 0 and H > 0 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be [{T}, {H}] with unit element stride")
+    return t.stride(0) if T > 1 else H
 
 
 def _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
@@ -104,9 +117,9 @@ def _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_no
     if prefix.dim() != 2:
         raise ValueError("prefix must be [T, H]")
     T, H = prefix.shape
-    _rows("prefix", prefix, T, H, True)
-    _rows("delta", delta, T, H, False)
-    _rows("out", out, T, H, True)
+    ps = _rows("prefix", prefix, T, H, True)
+    ds = _rows("delta", delta, T, H, False)
+    os_ = _rows("out", out, T, H, True)
     for name, w in (("res_w", res_w), ("rms_w", rms_w), ("output_norm_weight", output_norm_weight)):
         if w is None:
             if name != "output_norm_weight":
@@ -124,9 +137,25 @@ def _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_no
                 (blocks.numel() > 0 and blocks.stride(2) != 1):
             raise ValueError(f"blocks must be [{T}, capacity, {H}] with unit element stride")
         ts, ss, cap = blocks.stride(0), blocks.stride(1), blocks.shape[1]
-    return (_ptr(prefix), _ptr(delta), _ptr(blocks), ts, ss, cap, int(num_blocks), _ptr(res_w),
-            _ptr(rms_w), float(rms_eps), _ptr(output_norm_weight), float(output_norm_eps),
-            int(block_write_idx), _ptr(out), T, H)
+    return dict(prefix=_ptr(prefix), ps=ps, delta=_ptr(delta), ds=ds, blocks=_ptr(blocks), ts=ts,
+                ss=ss, cap=cap, nb=int(num_blocks), res_w=_ptr(res_w), rms_w=_ptr(rms_w),
+                eps=float(rms_eps), onw=_ptr(output_norm_weight), oeps=float(output_norm_eps),
+                widx=int(block_write_idx), out=_ptr(out), os=os_, T=T, H=H)
+
+
+def _dense_args(m):
+    return (m["prefix"], m["delta"], m["blocks"], m["ts"], m["ss"], m["cap"], m["nb"], m["res_w"],
+            m["rms_w"], m["eps"], m["onw"], m["oeps"], m["widx"], m["out"], m["T"], m["H"])
+
+
+def _strided_args(m):
+    return (m["prefix"], m["ps"], m["delta"], m["ds"], m["blocks"], m["ts"], m["ss"], m["cap"],
+            m["nb"], m["res_w"], m["rms_w"], m["eps"], m["onw"], m["oeps"], m["widx"], m["out"],
+            m["os"], m["T"], m["H"])
+
+
+def _dense(m) -> bool:
+    return m["ps"] == m["H"] and m["ds"] == m["H"] and m["os"] == m["H"]
 
 
 def attnres_fwd(prefix: torch.Tensor, delta: Optional[torch.Tensor],
@@ -137,23 +166,31 @@ def attnres_fwd(prefix: torch.Tensor, delta: Optional[torch.Tensor],
                 stream: Optional[torch.cuda.Stream] = None, path: Optional[int] = None) -> None:
     """Enqueues the AttnRes forward on `stream` (default: the current stream).
 
-    prefix, delta, out: [T, H]; blocks: [T, capacity, H] (any token/slot
-    strides); weights: [H].  prefix (with a delta) and blocks[:, block_write_idx]
-    are updated in place.  `path` forces ATTNRES_PATH_ROW / ATTNRES_PATH_SPLIT.
+    prefix, delta, out: [T, H] with unit element stride and any row stride
+    (dense rows go through attnres_fwd / attnres_fwd_path, others through
+    attnres_fwd_strided); blocks: [T, capacity, H] (any token/slot strides);
+    weights: [H].  prefix (with a delta) and blocks[:, block_write_idx] are
+    updated in place.  `path` forces one of the ATTNRES_PATH_* kernels.
     """
-    args = _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
-                    output_norm_eps, block_write_idx, out)
+    m = _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
+                 output_norm_eps, block_write_idx, out)
     dev = prefix.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU")
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
-        if path is None:
-            rc = _lib.attnres_fwd(*args, s.cuda_stream)
+        if not _dense(m):
+            rc = _lib.attnres_fwd_strided(*_strided_args(m), s.cuda_stream,
+                                          ATTNRES_PATH_AUTO if path is None else int(path))
+            where = "attnres_fwd_strided"
+        elif path is None:
+            rc = _lib.attnres_fwd(*_dense_args(m), s.cuda_stream)
+            where = "attnres_fwd"
         else:
-            rc = _lib.attnres_fwd_path(*args, s.cuda_stream, int(path))
+            rc = _lib.attnres_fwd_path(*_dense_args(m), s.cuda_stream, int(path))
+            where = "attnres_fwd_path"
     if rc != ATTNRES_OK:
-        raise AttnResError(rc, "attnres_fwd")
+        raise AttnResError(rc, where)
 
 
 def attnres_fwd_path(*args, path: int, **kw) -> None:
@@ -164,9 +201,11 @@ def attnres_fwd_path(*args, path: int, **kw) -> None:
 def attnres_validate(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps,
                      output_norm_weight, output_norm_eps, block_write_idx, out) -> int:
     """The library's host-side checks alone; returns the status code."""
-    return _lib.attnres_validate(*_marshal(prefix, delta, blocks, num_blocks, res_w, rms_w,
-                                           rms_eps, output_norm_weight, output_norm_eps,
-                                           block_write_idx, out))
+    m = _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
+                 output_norm_eps, block_write_idx, out)
+    if _dense(m):
+        return _lib.attnres_validate(*_dense_args(m))
+    return _lib.attnres_validate_strided(*_strided_args(m))
 
 
 def attnres_init(device: Optional[int] = None) -> None:

@@ -8,14 +8,19 @@
 
 namespace attnres {
 
-constexpr int kHidden = 7168;          // the only hidden size the kernels are built for
+constexpr int kHidden = 7168;          // the hidden size of the tuned row and split kernels
+constexpr int kMaxHidden = ATTNRES_MAX_HIDDEN;  // largest H of the any-H row kernel
 constexpr int kMaxBlocks = 8;          // bank rows a token may mix
 constexpr int64_t kMaxTokens = 2147483647LL;   // grid.x limit of the row path
 constexpr int64_t kMaxStride = int64_t(1) << 46;
 
+// Row strides (prefix_stride, delta_stride, out_stride) are in elements and
+// ignored when T <= 1.
 struct FwdArgs {
   const void *prefix = nullptr;
+  int64_t prefix_stride = 0;
   const void *delta = nullptr;
+  int64_t delta_stride = 0;
   const void *blocks = nullptr;
   int64_t block_token_stride = 0;
   int64_t block_slot_stride = 0;
@@ -28,11 +33,14 @@ struct FwdArgs {
   float output_norm_eps = 0.f;
   int block_write_idx = -1;
   const void *out = nullptr;
+  int64_t out_stride = 0;
   int64_t T = 0;
   int64_t H = 0;
 };
 
 int validate(const FwdArgs &a);
+// The row stride actually used for a [T, H] matrix argument.
+inline int64_t row_stride(int64_t given, int64_t T, int64_t H) { return T <= 1 ? H : given; }
 const char *strerror_text(int status);
 
 }  // namespace attnres

@@ -4,31 +4,36 @@
 // The operation is defined in include/attnres.h (vllm-ascend PR #14840,
 // "Implementation walkthrough"; prhub digest of vLLM PR #54261, kernel
 // snippet under "Key source snippets").  The work is a streaming reduction:
-// per token it reads num_blocks + 1 (+1 with a delta) rows of 7168 bf16 once,
+// per token it reads num_blocks + 1 (+1 with a delta) rows of H bf16 once,
 // reduces each row to two scalars, and writes 1-3 rows.  Arithmetic intensity
 // is about 2 flop/byte, far below the fp32 ridge, so HBM bandwidth bounds it
 // and no matrix core is involved.
 //
-// Layout of the work: a "segment" is 8 consecutive bf16 (16 bytes); a row is
-// 896 segments.  A lane owns one segment of every source row of its token, so
-// each row is read with one 128-bit load per lane and the whole token stays in
-// VGPRs between the reduction and the mixture (no second read of any row).
+// Layout of the work: a "segment" is 8 consecutive bf16 (16 bytes); a row of
+// 7168 is 896 segments.  A lane owns one or more segments of every source row
+// of its token, so each row is read with 128-bit loads and the whole token
+// stays in VGPRs between the reduction and the mixture (no second read).
 //
-//  * Row path (many tokens): one 896-lane workgroup (14 waves) per token.
-//    Per-lane fp32 sum-of-squares and query dot for every source, a wave64
-//    DPP reduction, a cross-wave reduction through LDS, logits, the softmax
-//    normaliser in online form, the fp32 mixture, the optional output RMSNorm
-//    (a second LDS reduction), bf16 round-to-nearest-even stores.
-//  * Split path (few tokens): 14 single-wave workgroups per token, each owning
-//    512 elements of every row, so a single token is spread over 14 CUs.
-//    Partial sums are exchanged through a small device workspace with
-//    agent-scope release/acquire atomics (the 8 XCDs do not share L2) and a
-//    monotonic per-token arrival counter, so no reset is needed between calls
-//    or graph replays.  Waits are bounded: a wait that gives up raises a
-//    device flag instead of hanging.
+//  * Row path (H = 7168, many tokens): one 448-lane workgroup (7 waves, two
+//    segments per lane) per token.  Per-lane fp32 sum-of-squares and query
+//    dot of every source (packed bf16 dot products), a 16-lane DPP reduction,
+//    a cross-row reduction through LDS, logits, the softmax normaliser in
+//    online form, the fp32 mixture, the optional output RMSNorm (a second LDS
+//    reduction), bf16 round-to-nearest-even stores.
+//  * Split path (H = 7168, few tokens): 14 single-wave workgroups per token,
+//    each owning 512 elements of every row, so one token is spread over 14
+//    CUs.  Per-part sums (and, with an output norm, the sources' Gram matrix)
+//    are exchanged once through a device workspace of self-validating tagged
+//    words read and written with agent-scope atomics (the 8 XCDs do not share
+//    L2); no reset is needed between calls or graph replays.  Waits are
+//    bounded: a wait that gives up raises a device flag instead of hanging.
+//  * Any-H row path (other hidden sizes, multiples of 8 up to 16384): the row
+//    path's steps with a runtime row length, 64-512 lanes per token and two
+//    or four segments per lane; segments past the row end are masked.
 //
 // Compile-time specialisation on num_blocks (0..8), delta and output norm;
-// block_write_idx stays a uniform runtime branch.
+// block_write_idx stays a uniform runtime branch.  Row strides of prefix,
+// delta and out are runtime values.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -102,12 +107,17 @@ struct KParams {
   const uint16_t *rms_w;
   const uint16_t *onw;
   uint16_t *out;
-  int64_t tok_stride;
+  int64_t tok_stride;     // bank, elements
   int64_t slot_stride;
+  int64_t prefix_stride;  // row strides, elements
+  int64_t delta_stride;
+  int64_t out_stride;
   float rms_eps;
   float out_eps;
   int widx;
   int T;
+  int nseg;               // segments per row (H / 8); the any-H kernel's row length
+  float inv_h;            // 1 / H
   uint64_t *ws_part;
   unsigned *ws_flag;
 };
@@ -190,36 +200,68 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 // while the rows are still in flight), then the bank rows, prefix and delta.
 // Row bases are workgroup-uniform (scalar registers); lanes add their
 // 16-byte segment offsets.
-template <int NB, bool DELTA, bool ONORM, int SPL>
+//
+// MASKED (rows whose length is not a multiple of the workgroup's reach):
+// a segment at or past p.nseg loads nothing and holds zeros, which add
+// nothing to any sum, and is never stored.
+template <int NB, bool DELTA, bool ONORM, int SPL, bool MASKED = false>
 struct Token {
   static constexpr int NS = NB + 1;
   u32x4 rms[SPL], res[SPL], onw[SPL];  // weights
   u32x4 x[NS][SPL];                    // bank slots 0..NB-1, then prefix (cur after finish_cur)
   u32x4 d[SPL];                        // delta
 
+  __device__ __forceinline__ static bool in_row(const KParams &p, int seg) {
+    return !MASKED || seg < p.nseg;
+  }
+  __device__ __forceinline__ static u32x4 load_row(const uint16_t *q, bool ok) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (!MASKED) return load_stream(q);
+    return ok ? load_stream(q) : zero;
+  }
+  __device__ __forceinline__ static u32x4 load_weight(const uint16_t *q, bool ok) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (!MASKED) return load_cached(q);
+    return ok ? load_cached(q) : zero;
+  }
+
   __device__ __forceinline__ void issue(const KParams &p, int64_t t, int seg0, int seg_step) {
+    bool ok[SPL];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) ok[i] = in_row(p, seg0 + i * seg_step);
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
       const int off = (seg0 + i * seg_step) * kSeg;
-      rms[i] = load_cached(p.rms_w + off);
-      res[i] = load_cached(p.res_w + off);
-      if constexpr (ONORM) onw[i] = load_cached(p.onw + off);
+      rms[i] = load_weight(p.rms_w + off, ok[i]);
+      res[i] = load_weight(p.res_w + off, ok[i]);
     }
     const uint16_t *bank = p.blocks + t * p.tok_stride;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < SPL; ++i)
-        x[j][i] = load_stream(bank + j * p.slot_stride + (seg0 + i * seg_step) * kSeg);
+        x[j][i] = load_row(bank + j * p.slot_stride + (seg0 + i * seg_step) * kSeg, ok[i]);
 #pragma unroll
     for (int i = 0; i < SPL; ++i)
-      x[NB][i] = load_stream(p.prefix + t * kHidden + (seg0 + i * seg_step) * kSeg);
+      x[NB][i] = load_row(p.prefix + t * p.prefix_stride + (seg0 + i * seg_step) * kSeg, ok[i]);
     if constexpr (DELTA)
 #pragma unroll
       for (int i = 0; i < SPL; ++i)
-        d[i] = load_stream(p.delta + t * kHidden + (seg0 + i * seg_step) * kSeg);
+        d[i] = load_row(p.delta + t * p.delta_stride + (seg0 + i * seg_step) * kSeg, ok[i]);
     // Keep the scheduler from sinking any of these loads below the arithmetic.
     __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // The output-norm weight is needed only by the final store: loading it once
+  // the logits are known (an L2 hit) keeps it out of the registers that hold
+  // the rows during the reductions.
+  __device__ __forceinline__ void issue_onw(const KParams &p, int seg0, int seg_step) {
+    if constexpr (ONORM)
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int seg = seg0 + i * seg_step;
+        onw[i] = load_weight(p.onw + seg * kSeg, in_row(p, seg));
+      }
   }
 
   // Fused query q = rms_w * res_w, split exactly into two packed bf16 words:
@@ -310,9 +352,10 @@ struct Token {
                                             int seg_step) const {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
+      if (!in_row(p, seg0 + i * seg_step)) continue;
       const int64_t off = int64_t(seg0 + i * seg_step) * kSeg;
       if constexpr (DELTA)
-        store_stream<ATTNRES_NT_STORE_CUR>(p.prefix + t * kHidden + off, x[NB][i]);
+        store_stream<ATTNRES_NT_STORE_CUR>(p.prefix + t * p.prefix_stride + off, x[NB][i]);
       if (p.widx >= 0)
         store_stream<ATTNRES_NT_STORE_CUR>(
             p.blocks + t * p.tok_stride + p.widx * p.slot_stride + off, x[NB][i]);
@@ -325,6 +368,7 @@ struct Token {
                                         const float (&y)[SPL][8], float rsig) const {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
+      if (!in_row(p, seg0 + i * seg_step)) continue;
       const int64_t off = int64_t(seg0 + i * seg_step) * kSeg;
       u32x4 o;
 #pragma unroll
@@ -335,7 +379,7 @@ struct Token {
         else
           o[k] = pack_bf16x2(y[i][2 * k], y[i][2 * k + 1]);
       }
-      store_stream(p.out + t * kHidden + off, o);
+      store_stream(p.out + t * p.out_stride + off, o);
     }
     if (!ATTNRES_EARLY_CUR_STORE) store_cur(p, t, seg0, seg_step);
   }
@@ -365,7 +409,7 @@ __device__ __forceinline__ float softmax_lanes(float logit_lane) {
     z = z * __expf(m - mn) + __expf(l - mn);
     m = mn;
   }
-  return __expf(logit_lane - m) * (1.f / z);
+  return __expf(logit_lane - m) * __builtin_amdgcn_rcpf(z);  // z >= 1
 }
 
 // ---------------------------------------------------------------------------
@@ -412,13 +456,19 @@ attnres_row_kernel(KParams p) {
   constexpr bool kLoop = ATTNRES_ROW_WGS_PER_CU > 0;
   const int64_t t_step = kLoop ? int64_t(gridDim.x) : p.T;
   int par = 0;
+  // Segment i of a lane is lane + i * 448, so that each load instruction of a
+  // wave covers 1 KB of one row, whole cache lines.  (Adjacent segments per
+  // lane would save address registers but cover half lines per instruction,
+  // which measured 30% slower.)
+  const int seg0 = int(threadIdx.x);
+  const int seg_step = kRowThreads;
   for (int64_t t = blockIdx.x; t < p.T; t += t_step, par ^= 1) {
     Token<NB, DELTA, ONORM, SPL> tk;
-    tk.issue(p, t, threadIdx.x, kRowThreads);
+    tk.issue(p, t, seg0, seg_step);
     u32x4 qh[SPL], ql[SPL];
     tk.query(qh, ql);
     tk.finish_cur();
-    if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, threadIdx.x, kRowThreads);
+    if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, seg0, seg_step);
 
     float ss[NS], dq[NS];
     tk.partials(qh, ql, ss, dq);
@@ -436,6 +486,7 @@ attnres_row_kernel(KParams p) {
       }
     }
     __syncthreads();
+    tk.issue_onw(p, seg0, seg_step);
 
     float logit = 0.f;
     if (lane < NS) {
@@ -445,6 +496,7 @@ attnres_row_kernel(KParams p) {
     }
     const float p_lane = softmax_lanes<NS>(logit);
     float y[SPL][8];
+    tk.keep_packed();
     tk.mix(p_lane, y);
 
     float rsig = 1.f;
@@ -454,9 +506,112 @@ attnres_row_kernel(KParams p) {
       __syncthreads();
       rsig = rsqrtf(sum_row_partials(s_ysq[par]) * kInvHidden + p.out_eps);
     }
-    tk.store(p, t, threadIdx.x, kRowThreads, y, rsig);
+    tk.store(p, t, seg0, seg_step, y, rsig);
   }
 }
+
+// ---------------------------------------------------------------------------
+// any-H row path: one workgroup (1-8 waves) per token, runtime row length
+// ---------------------------------------------------------------------------
+
+constexpr int kAnyMaxThreads = 512;               // 8 waves
+constexpr int kAnyMaxRows = kAnyMaxThreads / 16;  // 16-lane row partials per workgroup
+
+// Sums n4 groups of four row partials in a fixed order.
+__device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
+  const float4 *v4 = reinterpret_cast<const float4 *>(v);
+  float s = 0.f;
+  for (int i = 0; i < n4; ++i) {
+    const float4 a = v4[i];
+    s += a.x;
+    s += a.y;
+    s += a.z;
+    s += a.w;
+  }
+  return s;
+}
+
+// The row path's steps for a runtime row of p.nseg segments: blockDim.x lanes
+// (whole waves, at most kAnyMaxThreads) with SPL segments each, blockDim.x *
+// SPL >= p.nseg.  With two segments per lane a token fits 128 VGPRs (four
+// waves per SIMD); four segments may take 256.
+template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kWave, kAnyMaxThreads),
+                               amdgpu_waves_per_eu(SPL <= 2 ? 4 : 2)))
+attnres_anyh_kernel(KParams p) {
+  constexpr int NS = NB + 1;
+  __shared__ __align__(16) float s_part[2 * NS][kAnyMaxRows];
+  __shared__ __align__(16) float s_ysq[kAnyMaxRows];
+
+  const int nthreads = blockDim.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int rowslot = wave * 4 + (lane >> 4);
+  const bool row_leader = (lane & 15) == 0;
+  const int n4 = nthreads / kWave;  // four row partials per wave
+  const int64_t t = blockIdx.x;
+  const int seg0 = int(threadIdx.x);  // whole-line loads, as in the row kernel
+  const int seg_step = nthreads;
+
+  Token<NB, DELTA, ONORM, SPL, MASKED> tk;
+  tk.issue(p, t, seg0, seg_step);
+  u32x4 qh[SPL], ql[SPL];
+  tk.query(qh, ql);
+  tk.finish_cur();
+
+  float ss[NS], dq[NS];
+  tk.partials(qh, ql, ss, dq);
+  tk.keep_packed();
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    ss[j] = row16_sum(ss[j]);
+    dq[j] = row16_sum(dq[j]);
+  }
+  if (row_leader) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      s_part[j][rowslot] = ss[j];
+      s_part[NS + j][rowslot] = dq[j];
+    }
+  }
+  __syncthreads();
+  tk.issue_onw(p, seg0, seg_step);
+
+  float logit = 0.f;
+  if (lane < NS) {
+    const float s = sum_row_partials_n(s_part[lane], n4);
+    const float d = sum_row_partials_n(s_part[NS + lane], n4);
+    logit = d * rsqrtf(s * p.inv_h + p.rms_eps);
+  }
+  const float p_lane = softmax_lanes<NS>(logit);
+  float y[SPL][8];
+  tk.keep_packed();
+  tk.mix(p_lane, y);
+
+  float rsig = 1.f;
+  if constexpr (ONORM) {
+    const float sy = row16_sum(sum_sq<SPL>(y));
+    if (row_leader) s_ysq[rowslot] = sy;
+    __syncthreads();
+    rsig = rsqrtf(sum_row_partials_n(s_ysq, n4) * p.inv_h + p.out_eps);
+  }
+  tk.store(p, t, seg0, seg_step, y, rsig);
+}
+
+// Launch shape of the any-H kernel for a row of nseg segments.
+struct AnyShape {
+  int spl;
+  int threads;
+  bool masked;
+};
+AnyShape anyh_shape(int64_t H) {
+  const int nseg = int(H / kSeg);
+  const int spl = nseg <= 2 * kAnyMaxThreads ? 2 : 4;
+  const int reach = kWave * spl;  // segments one wave covers
+  const int waves = (nseg + reach - 1) / reach;
+  return {spl, waves * kWave, nseg % reach != 0};
+}
+static_assert(4 * kAnyMaxThreads * kSeg >= kMaxHidden, "any-H kernel must reach the largest H");
 
 // ---------------------------------------------------------------------------
 // split path: kParts single-wave workgroups per token
@@ -597,6 +752,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     tagged_store(slot + lane, v, gen);
   }
 
+  tk.issue_onw(p, part * kPartThreads + lane, 0);
   // The token's totals: lane v holds word v summed over the parts.
   const float total = lane < NV ? gather(tok_ws, lane, gen, p.ws_flag) : 0.f;
   const int jl = lane < NS ? lane : 0;
@@ -605,6 +761,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   const float logit = lane < NS ? dq_j * rsqrtf(ss_j * kInvHidden + p.rms_eps) : 0.f;
   const float p_lane = softmax_lanes<NS>(logit);
   float y[1][8];
+  tk.keep_packed();
   tk.mix(p_lane, y);
 
   float rsig = 1.f;
@@ -651,6 +808,32 @@ template <int NB>
 KernelFn split_fn(bool d, bool o) {
   if (d) return o ? attnres_split_kernel<NB, true, true> : attnres_split_kernel<NB, true, false>;
   return o ? attnres_split_kernel<NB, false, true> : attnres_split_kernel<NB, false, false>;
+}
+
+template <int SPL, bool MASKED, int NB>
+KernelFn anyh_fn(bool d, bool o) {
+  if (d)
+    return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true>
+             : attnres_anyh_kernel<SPL, MASKED, NB, true, false>;
+  return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true>
+           : attnres_anyh_kernel<SPL, MASKED, NB, false, false>;
+}
+
+template <int NB>
+KernelFn anyh_pick(const AnyShape &sh, bool d, bool o) {
+  if (sh.spl == 2) return sh.masked ? anyh_fn<2, true, NB>(d, o) : anyh_fn<2, false, NB>(d, o);
+  return sh.masked ? anyh_fn<4, true, NB>(d, o) : anyh_fn<4, false, NB>(d, o);
+}
+
+KernelFn pick_anyh(const AnyShape &sh, int nb, bool d, bool o) {
+  switch (nb) {
+#define ATTNRES_CASE(N) \
+  case N: return anyh_pick<N>(sh, d, o);
+    ATTNRES_CASE(0) ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
+    ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
+#undef ATTNRES_CASE
+    default: return nullptr;
+  }
 }
 
 KernelFn pick(bool split, int nb, bool d, bool o) {
@@ -712,14 +895,20 @@ int init_device_locked(int device) {
 }
 
 int fwd_impl(const FwdArgs &a, void *stream, int path) {
-  if (path != ATTNRES_PATH_AUTO && path != ATTNRES_PATH_ROW && path != ATTNRES_PATH_SPLIT)
+  if (path != ATTNRES_PATH_AUTO && path != ATTNRES_PATH_ROW && path != ATTNRES_PATH_SPLIT &&
+      path != ATTNRES_PATH_ANY_H)
     return ATTNRES_E_PATH;
   int rc = validate(a);
   if (rc != ATTNRES_OK) return rc;
   if (a.T == 0) return ATTNRES_OK;
 
-  bool split = path == ATTNRES_PATH_SPLIT ||
-               (path == ATTNRES_PATH_AUTO && auto_split(a.T, a.num_blocks));
+  // The tuned kernels are built for H = 7168; every other H runs the any-H
+  // row kernel, which can also be forced at 7168.
+  const bool tuned = a.H == kHidden;
+  if (path == ATTNRES_PATH_SPLIT && !tuned) return ATTNRES_E_UNSUPPORTED;
+  const bool any_h = path == ATTNRES_PATH_ANY_H || !tuned;
+  const bool split = !any_h && (path == ATTNRES_PATH_SPLIT ||
+                                (path == ATTNRES_PATH_AUTO && auto_split(a.T, a.num_blocks)));
   if (split && a.T > ATTNRES_SPLIT_MAX_TOKENS) return ATTNRES_E_UNSUPPORTED;
 
   KParams kp{};
@@ -732,6 +921,11 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   kp.out = static_cast<uint16_t *>(const_cast<void *>(a.out));
   kp.tok_stride = a.block_token_stride;
   kp.slot_stride = a.block_slot_stride;
+  kp.prefix_stride = row_stride(a.prefix_stride, a.T, a.H);
+  kp.delta_stride = a.delta ? row_stride(a.delta_stride, a.T, a.H) : 0;
+  kp.out_stride = row_stride(a.out_stride, a.T, a.H);
+  kp.nseg = int(a.H / kSeg);
+  kp.inv_h = 1.0f / float(a.H);
   kp.rms_eps = a.rms_eps;
   kp.out_eps = a.output_norm_weight ? a.output_norm_eps : 0.f;
   kp.widx = a.block_write_idx;
@@ -756,12 +950,24 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
     kp.ws_flag = g_ws[dev].flag;
   }
 
-  KernelFn fn = pick(split, a.num_blocks, a.delta != nullptr, a.output_norm_weight != nullptr);
+  const bool has_d = a.delta != nullptr, has_o = a.output_norm_weight != nullptr;
+  hipError_t e;
+  if (any_h) {
+    const AnyShape sh = anyh_shape(a.H);
+    KernelFn fn = pick_anyh(sh, a.num_blocks, has_d, has_o);
+    if (!fn) return ATTNRES_E_NUM_BLOCKS;
+    void *args[] = {&kp};
+    e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(unsigned(a.T)),
+                        dim3(unsigned(sh.threads)), args, 0, s);
+    return e == hipSuccess ? ATTNRES_OK : hip_fail(e);
+  }
+
+  KernelFn fn = pick(split, a.num_blocks, has_d, has_o);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;
   unsigned row_grid = unsigned(a.T);
   if (!split && ATTNRES_ROW_WGS_PER_CU > 0) {
     int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
+    e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e);
     const int64_t cap = int64_t(cus) * ATTNRES_ROW_WGS_PER_CU;
@@ -770,18 +976,21 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   const dim3 grid = split ? dim3(unsigned(a.T) * kParts) : dim3(row_grid);
   const dim3 block = split ? dim3(kPartThreads) : dim3(kRowThreads);
   void *args[] = {&kp};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, args, 0, s);
+  e = hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, args, 0, s);
   if (e != hipSuccess) return hip_fail(e);
   return ATTNRES_OK;
 }
 
-FwdArgs make_args(const void *prefix, const void *delta, const void *blocks, int64_t ts,
-                  int64_t ss, int max_blocks, int num_blocks, const void *res_w,
-                  const void *rms_w, float rms_eps, const void *onw, float oeps, int widx,
-                  const void *out, int64_t T, int64_t H) {
+FwdArgs make_args(const void *prefix, int64_t prefix_stride, const void *delta,
+                  int64_t delta_stride, const void *blocks, int64_t ts, int64_t ss,
+                  int max_blocks, int num_blocks, const void *res_w, const void *rms_w,
+                  float rms_eps, const void *onw, float oeps, int widx, const void *out,
+                  int64_t out_stride, int64_t T, int64_t H) {
   FwdArgs a;
   a.prefix = prefix;
+  a.prefix_stride = prefix_stride;
   a.delta = delta;
+  a.delta_stride = delta_stride;
   a.blocks = blocks;
   a.block_token_stride = ts;
   a.block_slot_stride = ss;
@@ -794,6 +1003,7 @@ FwdArgs make_args(const void *prefix, const void *delta, const void *blocks, int
   a.output_norm_eps = oeps;
   a.block_write_idx = widx;
   a.out = out;
+  a.out_stride = out_stride;
   a.T = T;
   a.H = H;
   return a;
@@ -809,9 +1019,9 @@ extern "C" int attnres_fwd(void *prefix, const void *delta, void *blocks,
                            int num_blocks, const void *res_w, const void *rms_w, float rms_eps,
                            const void *output_norm_weight, float output_norm_eps,
                            int block_write_idx, void *out, int64_t T, int64_t H, void *stream) {
-  return fwd_impl(make_args(prefix, delta, blocks, block_token_stride, block_slot_stride,
+  return fwd_impl(make_args(prefix, H, delta, H, blocks, block_token_stride, block_slot_stride,
                             max_blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
-                            output_norm_eps, block_write_idx, out, T, H),
+                            output_norm_eps, block_write_idx, out, H, T, H),
                   stream, ATTNRES_PATH_AUTO);
 }
 
@@ -821,9 +1031,24 @@ extern "C" int attnres_fwd_path(void *prefix, const void *delta, void *blocks,
                                 const void *rms_w, float rms_eps, const void *output_norm_weight,
                                 float output_norm_eps, int block_write_idx, void *out, int64_t T,
                                 int64_t H, void *stream, int path) {
-  return fwd_impl(make_args(prefix, delta, blocks, block_token_stride, block_slot_stride,
+  return fwd_impl(make_args(prefix, H, delta, H, blocks, block_token_stride, block_slot_stride,
                             max_blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
-                            output_norm_eps, block_write_idx, out, T, H),
+                            output_norm_eps, block_write_idx, out, H, T, H),
+                  stream, path);
+}
+
+extern "C" int attnres_fwd_strided(void *prefix, int64_t prefix_stride, const void *delta,
+                                   int64_t delta_stride, void *blocks,
+                                   int64_t block_token_stride, int64_t block_slot_stride,
+                                   int max_blocks, int num_blocks, const void *res_w,
+                                   const void *rms_w, float rms_eps,
+                                   const void *output_norm_weight, float output_norm_eps,
+                                   int block_write_idx, void *out, int64_t out_stride, int64_t T,
+                                   int64_t H, void *stream, int path) {
+  return fwd_impl(make_args(prefix, prefix_stride, delta, delta_stride, blocks,
+                            block_token_stride, block_slot_stride, max_blocks, num_blocks, res_w,
+                            rms_w, rms_eps, output_norm_weight, output_norm_eps, block_write_idx,
+                            out, out_stride, T, H),
                   stream, path);
 }
 

@@ -9,10 +9,12 @@ round-to-nearest-even cast.
 Workload shapes follow the pages: hidden size 7168, at most 8 block residuals
 per token, single-token decode up to long prefill (vLLM PR #54261 digest,
 "Motivation" and "Risks and impact").  The pages benchmark on random inputs
-only, so no dataset is involved.
+only, so no dataset is involved.  Other hidden sizes use the same recipes.
 
 Layout conventions used everywhere:
-  * prefix, delta, out: [T, H] bf16, row stride H.
+  * prefix, delta, out: [T, H] bf16 values, held densely here; on the device
+    their rows may be placed ``row_pad`` elements apart beyond H (the gap
+    filled with a sentinel).
   * bank: one flat bf16 buffer; element (t, i, h) sits at
     ``t*token_stride + i*slot_stride + h``.  Token-major by default
     (slot_stride = H, token_stride = cap*H + token_pad); slot-major on request.
@@ -43,11 +45,16 @@ class Case:
     has_onorm: bool = True
     widx: int = -1
     token_pad: int = 0          # extra elements per token after the cap slots
+    row_pad: int = 0            # extra elements after each prefix/delta/out row on the device
     slot_major: bool = False    # bank laid out [cap, T, H] instead of [T, cap, H]
     recipe: str = "normal"      # normal | decode | student_t | soft
     seed: int = 0
     eps: float = 1e-6
     oeps: float = 1e-6
+
+    @property
+    def row_stride(self) -> int:
+        return self.H + self.row_pad
 
     @property
     def slot_stride(self) -> int:
@@ -141,7 +148,7 @@ def make_inputs(case: Case, chunk_tokens: int = 512) -> Inputs:
     w_res = 1.0 + 0.1 * torch.randn(H, generator=gen)
     if case.recipe == "soft":
         # soft-logit variant: sqrt(sum q^2) ~ 1 so the softmax is not one-hot
-        w_res = 0.0118 * torch.randn(H, generator=gen)
+        w_res = (0.0118 * (HIDDEN / H) ** 0.5) * torch.randn(H, generator=gen)
     res_w = _bits(_bf16(w_res))
     rms_w = _bits(_bf16(1.0 + 0.1 * torch.randn(H, generator=gen)))
     onw = _bits(_bf16(1.0 + 0.1 * torch.randn(H, generator=gen))) if case.has_onorm else None
@@ -235,6 +242,14 @@ def soft_logits(T: int = 64, nb: int = 8) -> Case:
     """Not one of the named workloads: scoring weights scaled so logits are
     O(1) and the mixture really mixes."""
     return Case(f"soft_T{T}_nb{nb}", T=T, nb=nb, widx=nb - 1, recipe="soft", seed=77)
+
+
+def other_hidden(H: int, T: int = 40, nb: int = 6, **kw) -> Case:
+    """Not one of the named workloads: the same recipe at another hidden
+    size (delta, output norm and a write into a source slot by default)."""
+    kw.setdefault("widx", nb - 1 if nb > 0 else -1)
+    kw.setdefault("seed", 1000 + H + T + nb)
+    return Case(f"hidden{H}_T{T}_nb{nb}", T=T, nb=nb, H=H, **kw)
 
 
 def with_(case: Case, **kw) -> Case:

@@ -34,13 +34,16 @@ def to_dev(a: Optional[np.ndarray]) -> Optional[torch.Tensor]:
 def from_dev(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
     if t is None:
         return None
-    return t.cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy().view(np.uint16)
+
+
+ROW_GAP_BITS = 0x7F83   # a NaN: fills the gaps between strided rows
 
 
 @dataclass
 class Dev:
     case: W.Case
-    prefix: torch.Tensor
+    prefix: torch.Tensor        # [T, H], row stride case.row_stride
     delta: Optional[torch.Tensor]
     bank: torch.Tensor          # flat
     bank3: torch.Tensor         # [T, cap, H] strided view
@@ -48,14 +51,31 @@ class Dev:
     rms_w: torch.Tensor
     onw: Optional[torch.Tensor]
     out: torch.Tensor
+    gaps: dict                  # name -> the full [T, row_stride] buffer of a strided matrix
+
+
+def _matrix(a: Optional[np.ndarray], c: W.Case, name: str, gaps: dict):
+    """A [T, H] matrix on the device: dense, or rows case.row_stride apart with
+    the gaps filled by ROW_GAP_BITS."""
+    if a is None:
+        return None
+    if c.row_pad == 0:
+        return to_dev(a)
+    full = torch.full((c.T, c.row_stride), ROW_GAP_BITS, dtype=torch.int16, device="cuda")
+    view = full[:, :c.H]
+    view.copy_(to_dev(a))
+    gaps[name] = full
+    return view
 
 
 def upload(inp: W.Inputs) -> Dev:
     c = inp.case
     bank = to_dev(inp.bank)
     bank3 = bank.as_strided((c.T, c.cap, c.H), (c.token_stride, c.slot_stride, 1))
-    return Dev(c, to_dev(inp.prefix), to_dev(inp.delta), bank, bank3, to_dev(inp.res_w),
-               to_dev(inp.rms_w), to_dev(inp.onw), to_dev(inp.out_init))
+    gaps = {}
+    return Dev(c, _matrix(inp.prefix, c, "prefix", gaps), _matrix(inp.delta, c, "delta", gaps),
+               bank, bank3, to_dev(inp.res_w), to_dev(inp.rms_w), to_dev(inp.onw),
+               _matrix(inp.out_init, c, "out", gaps), gaps)
 
 
 def run(d: Dev, path: Optional[int] = None, stream=None) -> None:
@@ -73,12 +93,15 @@ class Result:
     res_w: np.ndarray
     rms_w: np.ndarray
     onw: Optional[np.ndarray]
+    gaps_untouched: dict        # name -> whether every gap element still holds ROW_GAP_BITS
 
 
 def download(d: Dev) -> Result:
     torch.cuda.synchronize()
+    H = d.case.H
+    gaps = {name: bool((full[:, H:] == ROW_GAP_BITS).all().item()) for name, full in d.gaps.items()}
     return Result(from_dev(d.out), from_dev(d.prefix), from_dev(d.bank), from_dev(d.delta),
-                  from_dev(d.res_w), from_dev(d.rms_w), from_dev(d.onw))
+                  from_dev(d.res_w), from_dev(d.rms_w), from_dev(d.onw), gaps)
 
 
 def oracle_full(inp: W.Inputs):
@@ -125,6 +148,8 @@ def check_full(inp: W.Inputs, got: Result, ref) -> None:
 
 def check_inputs_untouched(inp: W.Inputs, got: Result) -> None:
     c = inp.case
+    for name, ok in got.gaps_untouched.items():
+        assert ok, f"{c.name}: the gap after a {name} row was written"
     if inp.delta is not None:
         assert (got.delta == inp.delta).all(), c.name + ": delta modified"
     assert (got.res_w == inp.res_w).all() and (got.rms_w == inp.rms_w).all(), c.name + ": weights modified"

@@ -5,6 +5,7 @@ calls never dereference a pointer)."""
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -50,6 +51,8 @@ def test_binding_status_table_matches_header(A):
     assert consts["ATTNRES_SPLIT_MAX_TOKENS"] == A.ATTNRES_SPLIT_MAX_TOKENS
     assert consts["ATTNRES_PATH_ROW"] == A.ATTNRES_PATH_ROW
     assert consts["ATTNRES_PATH_SPLIT"] == A.ATTNRES_PATH_SPLIT
+    assert consts["ATTNRES_PATH_ANY_H"] == A.ATTNRES_PATH_ANY_H == 3
+    assert consts["ATTNRES_MAX_HIDDEN"] == A.ATTNRES_MAX_HIDDEN
 
 
 def _args(**kw):
@@ -88,7 +91,11 @@ CASES = [
     ("negative_capacity", dict(cap=-1, nb=0), "ATTNRES_E_SHAPE"),
     ("too_many_tokens", dict(T=1 << 31), "ATTNRES_E_SHAPE"),
     ("huge_stride", dict(ts=1 << 50), "ATTNRES_E_SHAPE"),
-    ("other_hidden_size", dict(H=4096), "ATTNRES_E_UNSUPPORTED"),
+    ("valid_other_hidden_size", dict(H=4096), "ATTNRES_OK"),
+    ("valid_smallest_hidden", dict(H=8), "ATTNRES_OK"),
+    ("valid_largest_hidden", dict(H=16384, ts=8 * 16384, ss=16384), "ATTNRES_OK"),
+    ("hidden_not_multiple_of_8", dict(H=7164), "ATTNRES_E_UNSUPPORTED"),
+    ("hidden_above_max", dict(H=16392, ts=8 * 16392, ss=16392), "ATTNRES_E_UNSUPPORTED"),
     ("nb_negative", dict(nb=-1), "ATTNRES_E_NUM_BLOCKS"),
     ("nb_above_8", dict(nb=9, cap=10, ts=10 * H), "ATTNRES_E_NUM_BLOCKS"),
     ("nb_above_capacity", dict(nb=5, cap=4, ts=4 * H), "ATTNRES_E_NUM_BLOCKS"),
@@ -124,6 +131,75 @@ def test_validate(A, name, mod, expect):
     assert A.STATUS[rc] == expect
 
 
+def _validate_strided(A, a):
+    return A.lib().attnres_validate_strided(
+        a["prefix"], a.get("ps", a["H"]), a["delta"], a.get("ds", a["H"]), a["blocks"], a["ts"],
+        a["ss"], a["cap"], a["nb"], a["res_w"], a["rms_w"], a["eps"], a["onw"], a["oeps"], a["widx"],
+        a["out"], a.get("os", a["H"]), a["T"], a["H"])
+
+
+P0 = 0x10000000
+STRIDED_CASES = [
+    ("dense_strides", {}, "ATTNRES_OK"),
+    ("padded_rows", dict(ps=H + 64, ds=H + 128, os=2 * H), "ATTNRES_OK"),
+    # prefix and delta interleaved in one [T, 2H] buffer (prefix is written)
+    ("prefix_delta_interleaved", dict(delta=P0 + 2 * H, ps=2 * H, ds=2 * H), "ATTNRES_OK"),
+    ("out_interleaved_with_prefix", dict(out=P0 + 2 * H, ps=2 * H, os=2 * H), "ATTNRES_OK"),
+    ("out_interleaved_overlapping", dict(out=P0 + 2 * (H - 8), ps=2 * H, os=2 * H), "ATTNRES_E_ALIAS"),
+    ("out_other_stride_overlapping", dict(out=P0 + 2 * H, ps=2 * H, os=3 * H), "ATTNRES_E_ALIAS"),
+    ("delta_interleaved_overlapping", dict(delta=P0 + 2 * H - 16, ps=2 * H, ds=2 * H), "ATTNRES_E_ALIAS"),
+    ("row_stride_below_H", dict(ps=H - 8), "ATTNRES_E_STRIDE"),
+    ("row_stride_zero", dict(os=0), "ATTNRES_E_STRIDE"),
+    ("row_stride_negative", dict(ds=-H), "ATTNRES_E_STRIDE"),
+    ("row_stride_not_multiple_of_8", dict(os=H + 4), "ATTNRES_E_ALIGN"),
+    ("row_stride_huge", dict(ps=1 << 50), "ATTNRES_E_SHAPE"),
+    ("single_token_ignores_row_strides", dict(T=1, ps=0, ds=-5, os=3), "ATTNRES_OK"),
+    ("no_delta_ignores_its_stride", dict(delta=None, ds=3), "ATTNRES_OK"),
+]
+
+
+@pytest.mark.parametrize("name,mod,expect", STRIDED_CASES, ids=[c[0] for c in STRIDED_CASES])
+def test_validate_strided(A, name, mod, expect):
+    rc = _validate_strided(A, _args(**mod))
+    assert A.STATUS[rc] == expect
+
+
+def test_dense_validate_is_strided_validate_with_stride_H(A):
+    for _, mod, _ in CASES:
+        a = _args(**mod)
+        assert _validate(A, a) == _validate_strided(A, a), mod
+
+
+def test_row_overlap_check_against_brute_force(A):
+    """out (written) against prefix rows, both strided: the library must
+    reject every layout where some element is shared, and, when both have the
+    same row stride (or one has a single row), accept every layout where none
+    is.  Element sets are enumerated on the host."""
+    rng = np.random.default_rng(11)
+    h = 16
+    far = 0x7000000
+    checked_equal = 0
+    for _ in range(3000):
+        T = int(rng.integers(1, 6))
+        ps = h * int(rng.integers(1, 5)) if rng.random() < 0.7 else h + 8 * int(rng.integers(0, 6))
+        os_ = ps if rng.random() < 0.6 else h + 8 * int(rng.integers(0, 10))
+        off = 16 * int(rng.integers(-40, 40))       # byte offset of out from prefix
+        prefix, out = 0x1000000, 0x1000000 + off
+        pe = {prefix + 2 * (t * ps + k) for t in range(T) for k in range(h)}
+        oe = {out + 2 * (t * os_ + k) for t in range(T) for k in range(h)}
+        shared = bool(pe & oe)
+        a = dict(prefix=prefix, ps=ps, delta=None, ds=h, blocks=None, ts=0, ss=0, cap=0, nb=0,
+                 res_w=far, rms_w=far + 0x10000, eps=1e-6, onw=None, oeps=0.0, widx=-1, out=out,
+                 os=os_, T=T, H=h)
+        rc = _validate_strided(A, a)
+        if shared:
+            assert A.STATUS[rc] == "ATTNRES_E_ALIAS", (T, ps, os_, off)
+        elif ps == os_ or T == 1:
+            assert rc == 0, (T, ps, os_, off, A.STATUS[rc])
+            checked_equal += 1
+    assert checked_equal > 500
+
+
 def test_read_only_overlaps_are_allowed(A):
     # prefix read-only (no delta) may share memory with a read-only bank and
     # with the weights; only written buffers must be exclusive.
@@ -134,7 +210,7 @@ def test_read_only_overlaps_are_allowed(A):
 def test_fwd_rejects_before_any_gpu_work(A):
     """attnres_fwd runs the same checks first: an invalid call returns its
     code without touching the (fake) pointers or needing a GPU."""
-    a = _args(H=4096)
+    a = _args(H=7164)
     lib = A.lib()
     for fn, extra in ((lib.attnres_fwd, [None]), (lib.attnres_fwd_path, [None, A.ATTNRES_PATH_ROW])):
         rc = fn(a["prefix"], a["delta"], a["blocks"], a["ts"], a["ss"], a["cap"], a["nb"], a["res_w"],

@@ -13,6 +13,7 @@ import torch
 from kimi_k3_attention_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
+A_PATH_ANY_H = 3  # ATTNRES_PATH_ANY_H (checked against the header by the boundary tests)
 
 
 @pytest.fixture(scope="module")
@@ -23,10 +24,14 @@ def G():
     return gpu_harness
 
 
-def _paths(T):
+def _paths(T, H=7168):
+    """Every kernel that can run a call of T tokens at hidden size H: at 7168
+    the tuned row kernel, the split kernel (T <= 256) and the any-H kernel;
+    at other sizes the any-H kernel (through the automatic choice, the row
+    selector and its own)."""
     from kimi_k3_attention_amd import attnres as A
-    ps = [None, A.ATTNRES_PATH_ROW]
-    if T <= A.ATTNRES_SPLIT_MAX_TOKENS:
+    ps = [None, A.ATTNRES_PATH_ROW, A.ATTNRES_PATH_ANY_H]
+    if H == 7168 and T <= A.ATTNRES_SPLIT_MAX_TOKENS:
         ps.append(A.ATTNRES_PATH_SPLIT)
     return ps
 
@@ -40,7 +45,7 @@ def _run_and_check_all_paths(G, case, ref=None):
     inp = W.make_inputs(case)
     if ref is None:
         ref = G.oracle_full(inp)
-    for path in _paths(case.T):
+    for path in _paths(case.T, case.H):
         G.say(case.name, "path", path)
         d = G.upload(inp)
         G.run(d, path=path)
@@ -91,12 +96,84 @@ def test_long_prefill_sampled(G, T):
 def test_variant_matrix(G, case):
     inp = W.make_inputs(case)
     ref = G.oracle_full(inp)
-    paths = _paths(case.T) if case.T <= 256 else [None]
+    paths = _paths(case.T) if case.T <= 256 else [None, A_PATH_ANY_H]
     for path in paths:
         G.say(case.name, "path", path)
         d = G.upload(inp)
         G.run(d, path=path)
         G.check_full(inp, G.download(d), ref)
+
+
+# Hidden sizes other than 7168, run by the any-H kernel: two or four segments
+# per lane, rows that fill whole waves exactly and rows that need masking.
+HIDDEN_CASES = [
+    dict(H=8, T=9, nb=3),                 # one segment per row: 63 masked lanes
+    dict(H=1024, T=33, nb=8),
+    dict(H=2048, T=300, nb=4, has_onorm=False),
+    dict(H=2880, T=40, nb=7),             # 360 segments: masked, 3 waves
+    dict(H=4096, T=129, nb=8, widx=-1),
+    dict(H=5120, T=17, nb=0),
+    dict(H=7160, T=20, nb=5),             # one segment short of 7168
+    dict(H=8192, T=64, nb=8, has_delta=False),
+    dict(H=8200, T=12, nb=2),             # first size with four segments per lane
+    dict(H=12288, T=48, nb=6),
+    dict(H=16376, T=10, nb=8),            # 2047 segments: masked, 8 waves
+    dict(H=16384, T=24, nb=8, widx=0),
+]
+
+
+@pytest.mark.parametrize("kw", HIDDEN_CASES, ids=lambda kw: f"H{kw['H']}_T{kw['T']}_nb{kw['nb']}")
+def test_other_hidden_sizes(G, kw):
+    kw = dict(kw)
+    case = W.other_hidden(kw.pop("H"), kw.pop("T"), kw.pop("nb"), **kw)
+    _run_and_check_all_paths(G, case)
+
+
+def test_split_path_refuses_other_hidden_sizes(G):
+    from kimi_k3_attention_amd import attnres as A
+    case = W.other_hidden(4096, T=4, nb=2)
+    inp = W.make_inputs(case)
+    d = G.upload(inp)
+    with pytest.raises(A.AttnResError) as e:
+        G.run(d, path=A.ATTNRES_PATH_SPLIT)
+    assert e.value.name == "ATTNRES_E_UNSUPPORTED"
+    got = G.download(d)
+    assert (got.out == inp.out_init).all() and (got.prefix == inp.prefix).all()
+
+
+@pytest.mark.parametrize("H,T,nb", [(7168, 37, 5), (7168, 200, 8), (7168, 1, 8), (2880, 50, 4),
+                                    (16384, 9, 3)])
+def test_strided_rows(G, H, T, nb):
+    """prefix, delta and out rows placed row_pad elements apart (views into
+    wider buffers): every kernel reads and writes only the rows; the gaps keep
+    their sentinel."""
+    case = W.other_hidden(H, T, nb, row_pad=136, seed=300 + T)
+    _run_and_check_all_paths(G, case)
+
+
+def test_interleaved_prefix_delta_and_out(G):
+    """prefix and delta as the two halves of one [T, 2H] buffer (prefix is
+    written in place), out as every third row of a [3T, H] buffer."""
+    from kimi_k3_attention_amd import attnres as A
+    case = W.Case("interleaved_T45_nb6", T=45, nb=6, widx=2, seed=310)
+    inp = W.make_inputs(case)
+    ref = G.oracle_full(inp)
+    T, H = case.T, case.H
+    for path in _paths(T):
+        G.say(case.name, "path", path)
+        d = G.upload(inp)
+        pd = torch.cat([d.prefix, d.delta], dim=1).contiguous()     # [T, 2H]
+        outbuf = torch.full((3 * T, H), G.ROW_GAP_BITS, dtype=torch.int16, device="cuda")
+        out = outbuf[::3]
+        A.attnres_fwd(pd[:, :H], pd[:, H:], d.bank3, case.nb, d.res_w, d.rms_w, case.eps, d.onw,
+                      case.oeps, case.widx, out, path=path)
+        torch.cuda.synchronize()
+        G.assert_out_close(G.from_dev(out), ref.out_bits, case.name + " out")
+        assert (G.from_dev(pd[:, :H]) == ref.prefix_after).all(), "prefix after the call"
+        assert (G.from_dev(pd[:, H:]) == inp.delta).all(), "delta modified"
+        rest = torch.cat([outbuf[1::3], outbuf[2::3]])
+        assert (rest == G.ROW_GAP_BITS).all().item(), "out rows between the strided rows written"
+        assert (G.from_dev(d.bank) == ref.bank_after).all(), "bank after the call"
 
 
 def test_soft_logits_mix(G):
