@@ -260,6 +260,80 @@ def bench_hidden_sweep(Hs=HIDDEN_SWEEP, T: int = 1024, steps: int = 120):
     return res
 
 
+CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "bench_ceiling.so")
+# (name, row reads, row writes to a separate buffer, row writes in place) per token
+CEILING_CONFIGS = (("mid_prefill_10r_1w_2inplace", 10, 1, 2), ("10r_3w", 10, 3, 0),
+                   ("long_prefill_9r_1w", 9, 1, 0), ("read_only_10r", 10, 0, 0),
+                   ("copy_1r_1w", 1, 1, 0))
+
+
+def build_ceiling_probe(verbose: bool = False) -> str:
+    """Compiles bench_ceiling.hip (the memory-traffic probe) in-tree."""
+    import subprocess
+    from kimi_k3_attention_amd import build as kbuild
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [kbuild.HIPCC] + kbuild.FLAGS + ["-o", tmp, CEILING_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed on the ceiling probe:\n" + res.stderr[-4000:])
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
+
+
+def load_ceiling_probe():
+    import ctypes
+    if not os.path.exists(CEILING_LIB):
+        build_ceiling_probe()
+    lib = ctypes.CDLL(CEILING_LIB)
+    vp, i64, ci, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+    lib.ceiling_stream.argtypes = [vp, i64, vp, i64, ci, ci, ci, i64, u32, vp]
+    lib.ceiling_stream.restype = ci
+    return lib
+
+
+def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168):
+    """The traffic of a call without its arithmetic (bench_ceiling.hip), in the
+    row kernel's launch shape, over enough input sets to exceed the Infinity
+    Cache: the rate this access pattern reaches on the device.  Each
+    configuration moves about `call_bytes` per launch (the mid-prefill call's
+    bytes), so the token count differs between configurations."""
+    lib = load_ceiling_probe()
+    res = {}
+    for name, reads, wd, wi in CEILING_CONFIGS:
+        T = max(1, round(call_bytes / (2 * H * (reads + wd + wi))))
+        footprint = 2 * H * T * (reads + wd)
+        nsets = max(1, -(-2 * MALL_BYTES // footprint))
+        sets = []
+        for _ in range(nsets):
+            src = torch.randint(-30000, 30000, (T * reads * H,), dtype=torch.int16, device="cuda")
+            dst = torch.empty(max(T * wd * H, 8), dtype=torch.int16, device="cuda")
+            sets.append((src, dst))
+
+        def call(st):
+            rc = lib.ceiling_stream(st[0].data_ptr(), reads * H, st[1].data_ptr(), max(wd, 1) * H,
+                                    reads, wd, wi, T, 0x9E3779B9,
+                                    torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"ceiling probe {name} failed ({rc})")
+
+        calls = [lambda st=st: call(st) for st in sets]
+        for fn in calls:
+            fn()
+        torch.cuda.synchronize()
+        t = time_graph(calls, steps, replays=3)
+        us = pct([x / steps * 1e3 for x in t], 50)
+        nbytes = 2 * H * T * (reads + wd + wi)
+        res[name] = dict(T=T, us=round(us, 2), GBps=round(nbytes / us / 1e3, 1),
+                         frac=round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4))
+        log(f"ceiling probe {name}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(single_s: float = 8.0, multi_s: float = 1.5):
     """The fp64 oracle, as it stands, on the host, on whole mid-prefill calls
     (T=1024, 8 block rows): single-threaded for about single_s, then with the
@@ -427,7 +501,7 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--eager", action="store_true", help="plain launches instead of a hipGraph")
-    ap.add_argument("--only", choices=["mid", "decode"], default=None)
+    ap.add_argument("--only", choices=["mid", "decode", "ceiling"], default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--calibrate", action="store_true", help="run the known-size copy for counters")
     ap.add_argument("--hidden-sweep", action="store_true",
@@ -469,9 +543,12 @@ def main():
               flush=True)
         return
 
-    mid = None if args.only == "decode" else bench_mid(args.steps, args.warmup, args.eager)
-    decode = None if (args.only == "mid" or args.eager) else bench_decode(args.steps)
+    mid = None if args.only in ("decode", "ceiling") else bench_mid(args.steps, args.warmup,
+                                                                     args.eager)
+    decode = None if (args.only in ("mid", "ceiling") or args.eager) else bench_decode(args.steps)
     longp = None if (args.only or args.eager) else bench_long()
+    ceiling = (bench_ceiling() if (args.only == "ceiling" or (args.only is None and not args.eager))
+               else None)
     if A.attnres_device_status() != A.ATTNRES_OK:
         raise SystemExit("device wait flag raised during the benchmark")
     cpu = None if (args.no_cpu or args.only) else cpu_baseline()
@@ -504,6 +581,14 @@ def main():
                          "higher_is_better": False})
     if longp is not None:
         line["long_prefill"] = longp
+    if ceiling is not None:
+        probe = ceiling["mid_prefill_10r_1w_2inplace"]
+        line["traffic_ceiling"] = {
+            "probe": "same bytes and launch shape as the mid-prefill call (10 row reads, 1 row "
+                     "write, 2 in-place row writes per token), no arithmetic",
+            "GBps": probe["GBps"],
+            "kernel_fraction": None if mid is None else round(mid["gbps"] / probe["GBps"], 4),
+            "configs": ceiling}
     if cpu is not None:
         line["cpu_baseline"] = cpu
     line["kernel_source_hash"] = kernel_source_hash()

@@ -1,0 +1,110 @@
+// Memory-traffic ceiling probe for bench.py (measurement only, not part of
+// libattnres).
+//
+// One launch moves exactly the row traffic of an attention-residual call with
+// hidden size 7168: per token R row reads, then WI row writes back into rows
+// it has just read (the in-place prefix / bank-slot writes) and WD row writes
+// to a separate buffer (the output), in the row kernel's launch shape: one
+// 448-lane workgroup per token, two 16-byte segments per lane at lane and
+// lane + 448 (whole cache lines per instruction), 128-bit non-temporal loads
+// and stores.  The only arithmetic is an XOR fold that keeps every load live.
+// Its rate is what this access pattern reaches on the device, the reference
+// point for the library's kernels.
+//
+//   src: element (t, r, h) at src[t * src_token_stride + r * 7168 + h], r < R
+//   dst: element (t, w, h) at dst[t * dst_token_stride + w * 7168 + h], w < WD
+//   in-place row k < WI of token t (source row k) receives
+//       XOR of source rows k and R-1;
+//   dst row w of token t receives XOR of all R source rows, rotated by w bits.
+// With no writes at all, a lane whose XOR equals `never` (a value the caller
+// picks so that it does not occur) would store it to dst[0]: the loads stay
+// live without adding traffic.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowSegs = 896;  // 16-byte segments in a row of 7168 bf16
+constexpr int kThreads = 448;
+constexpr int kSpl = 2;
+
+__device__ __forceinline__ u32x4 ld(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ u32x4 rotl(u32x4 v, int s) {
+  if (s == 0) return v;
+  return (v << s) | (v >> (32 - s));
+}
+
+template <int R, int WD, int WI>
+__global__ void __launch_bounds__(kThreads) ceiling_kernel(u32x4 *src, int64_t src_stride,
+                                                           u32x4 *dst, int64_t dst_stride,
+                                                           uint32_t never) {
+  static_assert(WI <= R, "in-place rows must be source rows");
+  const int64_t t = blockIdx.x;
+  u32x4 *s = src + t * src_stride;
+  u32x4 *d = dst + t * dst_stride;
+  u32x4 x[R][kSpl];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < kSpl; ++i) x[r][i] = ld(s + r * kRowSegs + threadIdx.x + i * kThreads);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kSpl; ++i) {
+    const int seg = threadIdx.x + i * kThreads;
+    u32x4 acc = x[0][i];
+#pragma unroll
+    for (int r = 1; r < R; ++r) acc ^= x[r][i];
+#pragma unroll
+    for (int w = 0; w < WD; ++w) st(d + w * kRowSegs + seg, rotl(acc, w));
+#pragma unroll
+    for (int k = 0; k < WI; ++k) st(s + k * kRowSegs + seg, x[k][i] ^ x[R - 1][i]);
+    if constexpr (WD == 0 && WI == 0) {
+      if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == never) dst[0] = acc;
+    }
+  }
+}
+
+typedef void (*Fn)(u32x4 *, int64_t, u32x4 *, int64_t, uint32_t);
+
+Fn pick(int reads, int wd, int wi) {
+#define CEIL_CASE(R, D, I) \
+  if (reads == R && wd == D && wi == I) return ceiling_kernel<R, D, I>;
+  CEIL_CASE(10, 1, 2)  // mid prefill: 8 bank rows + prefix + delta; out; prefix and bank slot
+  CEIL_CASE(10, 3, 0)  // the same bytes, every write to a separate buffer
+  CEIL_CASE(9, 1, 0)   // long prefill: 8 bank rows + prefix; out
+  CEIL_CASE(10, 0, 0)  // reads only
+  CEIL_CASE(1, 1, 0)   // copy
+#undef CEIL_CASE
+  return nullptr;
+}
+
+}  // namespace
+
+// Returns 0 on success, -1 for an unsupported (reads, writes) combination or
+// bad sizes / alignment, -2 if the launch failed.  Asynchronous on `stream`.
+// dst must hold at least 16 bytes even when dst_writes == 0.
+extern "C" int ceiling_stream(void *src, int64_t src_token_stride, void *dst,
+                              int64_t dst_token_stride, int reads, int dst_writes,
+                              int inplace_writes, int64_t T, uint32_t never, void *stream) {
+  Fn fn = pick(reads, dst_writes, inplace_writes);
+  if (!fn || T < 0 || T > 0x7fffffff) return -1;
+  if (T == 0) return 0;
+  if (!src || !dst) return -1;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return -1;
+  if (src_token_stride % 8 != 0 || dst_token_stride % 8 != 0) return -1;
+  if (src_token_stride < int64_t(reads) * 7168 ||
+      (dst_writes > 0 && dst_token_stride < int64_t(dst_writes) * 7168))
+    return -1;
+  void *args_src = src;
+  void *args_dst = dst;
+  int64_t ss = src_token_stride / 8, ds = dst_token_stride / 8;  // in 16-byte segments
+  void *args[] = {&args_src, &ss, &args_dst, &ds, &never};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(unsigned(T)),
+                                 dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : -2;
+}
