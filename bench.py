@@ -334,6 +334,24 @@ def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168):
     return res
 
 
+def _host_cpu() -> dict:
+    """The host's CPU model and logical CPU counts (reported with the CPU leg)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = None
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(single_s: float = 8.0, multi_s: float = 1.5):
     """The fp64 oracle, as it stands, on the host, on whole mid-prefill calls
     (T=1024, 8 block rows): single-threaded for about single_s, then with the
@@ -382,7 +400,7 @@ def cpu_baseline(single_s: float = 8.0, multi_s: float = 1.5):
                        f"calls, {dt1 * 1e3:.0f} ms/call",
                 single_thread=dict(value=round(gbps1, 4), unit="GB/s", cores=1,
                                    ms_per_call=round(dt1 * 1e3, 1)),
-                ms_per_call=round(dtn * 1e3, 1))
+                ms_per_call=round(dtn * 1e3, 1), host=_host_cpu())
 
 
 def load_traffic():

@@ -84,12 +84,6 @@ constexpr int kPartThreads = kSegs / kParts;  // 64 = one wave
 constexpr int kSlot = 64;                     // 64-bit words per (token, part) workspace slot
 constexpr int kSlotYsq = kSlot - 1;           // where a part's sum of y^2 goes
 constexpr int kSpinLimit = 1 << 20;           // bounded cross-workgroup wait
-// attnres_fwd's choice of kernel, from measured latency per call: spreading a
-// token over 14 CUs (split) beats one CU per token (row) while the grid is
-// small, the more so the more block rows a token has.
-__host__ __device__ constexpr bool auto_split(int64_t T, int nb) {
-  return T <= 16 || (T <= 32 && nb >= 2) || (T <= 64 && nb >= 7);
-}
 constexpr float kInvHidden = 1.0f / kHidden;
 
 static_assert(kSegs * kSeg == kHidden, "hidden size must be a multiple of 8");
@@ -118,7 +112,7 @@ struct KParams {
   int T;
   int nseg;               // segments per row (H / 8); the any-H kernel's row length
   float inv_h;            // 1 / H
-  uint64_t *ws_part;
+  uint64_t *ws_part;       // split path: tagged words, 14 parts per token
   unsigned *ws_flag;
 };
 
@@ -687,6 +681,44 @@ struct SplitWords {
 // squares of y is exchanged directly instead.
 constexpr float kGramGuard = 1.f / 16.f;
 
+// The mixture weights from a token's exchanged totals (lane v < NV holds word
+// v): lane j < NS returns p_j; ss_j receives lane j's sum of squares.
+template <int NS, bool ONORM>
+__device__ __forceinline__ float weights_from_totals(float total, float rms_eps, float &ss_j) {
+  using Words = SplitWords<NS, ONORM>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int jl = lane < NS ? lane : 0;
+  ss_j = lane_shuffle(total, Words::ss_word(jl));
+  const float dq_j = lane_shuffle(total, Words::kDot + jl);
+  const float logit = lane < NS ? dq_j * rsqrtf(ss_j * kInvHidden + rms_eps) : 0.f;
+  return softmax_lanes<NS>(logit);
+}
+
+// ||y||^2 = sum_jk c_jk p_j p_k G_jk from the Gram words of the totals (c = 1
+// on the diagonal, 2 off it), and its guard bound b = sum_j p_j ||x_j||; both
+// wave-uniform.  The Gram form is used only when ysq >= kGramGuard * b^2.
+template <int NS>
+__device__ __forceinline__ void gram_ysq(float total, float p_lane, float ss_j, float &ysq,
+                                         float &b) {
+  using Words = SplitWords<NS, true>;
+  const int lane = threadIdx.x & (kWave - 1);
+  // Lane w < kPairs holds G_jk for the w-th pair (j <= k).
+  int j = 0, rem = lane;
+#pragma unroll
+  for (int r = 0; r < NS; ++r)
+    if (rem >= NS - j && j < NS - 1) {
+      rem -= NS - j;
+      ++j;
+    }
+  const int k = j + rem;
+  const float pj = lane_shuffle(p_lane, j);
+  const float pk = lane_shuffle(p_lane, k < NS ? k : 0);
+  const float term = lane < Words::kPairs ? (j == k ? 1.f : 2.f) * pj * pk * total : 0.f;
+  const float bound = lane < NS ? p_lane * sqrtf(fmaxf(ss_j, 0.f)) : 0.f;
+  ysq = lane_value(wave_sum_lane63(term), kWave - 1);
+  b = lane_value(wave_sum_lane63(bound), kWave - 1);
+}
+
 template <int NB, bool DELTA, bool ONORM>
 __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) {
   constexpr int NS = NB + 1;
@@ -755,32 +787,16 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   tk.issue_onw(p, part * kPartThreads + lane, 0);
   // The token's totals: lane v holds word v summed over the parts.
   const float total = lane < NV ? gather(tok_ws, lane, gen, p.ws_flag) : 0.f;
-  const int jl = lane < NS ? lane : 0;
-  const float ss_j = lane_shuffle(total, Words::ss_word(jl));
-  const float dq_j = lane_shuffle(total, Words::kDot + jl);
-  const float logit = lane < NS ? dq_j * rsqrtf(ss_j * kInvHidden + p.rms_eps) : 0.f;
-  const float p_lane = softmax_lanes<NS>(logit);
+  float ss_j;
+  const float p_lane = weights_from_totals<NS, ONORM>(total, p.rms_eps, ss_j);
   float y[1][8];
   tk.keep_packed();
   tk.mix(p_lane, y);
 
   float rsig = 1.f;
   if constexpr (ONORM) {
-    // Lane w < kPairs holds G_jk for the w-th pair (j <= k).
-    int j = 0, rem = lane;
-#pragma unroll
-    for (int r = 0; r < NS; ++r)
-      if (rem >= NS - j && j < NS - 1) {
-        rem -= NS - j;
-        ++j;
-      }
-    const int k = j + rem;
-    const float pj = lane_shuffle(p_lane, j);
-    const float pk = lane_shuffle(p_lane, k < NS ? k : 0);
-    const float term = lane < Words::kPairs ? (j == k ? 1.f : 2.f) * pj * pk * total : 0.f;
-    const float bound = lane < NS ? p_lane * sqrtf(fmaxf(ss_j, 0.f)) : 0.f;
-    const float ysq = lane_value(wave_sum_lane63(term), kWave - 1);
-    const float b = lane_value(wave_sum_lane63(bound), kWave - 1);
+    float ysq, b;
+    gram_ysq<NS>(total, p_lane, ss_j, ysq, b);
     float tot = ysq;
     if (!(ysq >= kGramGuard * b * b)) {
       // Every part sees the same totals and takes the same branch.
@@ -836,10 +852,20 @@ KernelFn pick_anyh(const AnyShape &sh, int nb, bool d, bool o) {
   }
 }
 
-KernelFn pick(bool split, int nb, bool d, bool o) {
+enum class Kind { kRow, kSplit, kAnyH };
+
+// attnres_fwd's choice of kernel at H = 7168, from measured latency per call:
+// spreading a token over 14 CUs (split) beats one CU per token (row) while
+// the grid is small, the more so the more block rows a token has.
+Kind auto_kind(int64_t T, int nb) {
+  if (T <= 16 || (T <= 32 && nb >= 2) || (T <= 64 && nb >= 7)) return Kind::kSplit;
+  return Kind::kRow;
+}
+
+KernelFn pick(Kind kind, int nb, bool d, bool o) {
   switch (nb) {
 #define ATTNRES_CASE(N) \
-  case N: return split ? split_fn<N>(d, o) : row_fn<N>(d, o);
+  case N: return kind == Kind::kSplit ? split_fn<N>(d, o) : row_fn<N>(d, o);
     ATTNRES_CASE(0) ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
     ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
 #undef ATTNRES_CASE
@@ -906,9 +932,17 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   // row kernel, which can also be forced at 7168.
   const bool tuned = a.H == kHidden;
   if (path == ATTNRES_PATH_SPLIT && !tuned) return ATTNRES_E_UNSUPPORTED;
-  const bool any_h = path == ATTNRES_PATH_ANY_H || !tuned;
-  const bool split = !any_h && (path == ATTNRES_PATH_SPLIT ||
-                                (path == ATTNRES_PATH_AUTO && auto_split(a.T, a.num_blocks)));
+  Kind kind;
+  if (path == ATTNRES_PATH_ANY_H || !tuned)
+    kind = Kind::kAnyH;
+  else if (path == ATTNRES_PATH_SPLIT)
+    kind = Kind::kSplit;
+  else if (path == ATTNRES_PATH_ROW)
+    kind = Kind::kRow;
+  else
+    kind = auto_kind(a.T, a.num_blocks);
+  const bool any_h = kind == Kind::kAnyH;
+  const bool split = kind == Kind::kSplit;
   if (split && a.T > ATTNRES_SPLIT_MAX_TOKENS) return ATTNRES_E_UNSUPPORTED;
 
   KParams kp{};
@@ -962,10 +996,10 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
     return e == hipSuccess ? ATTNRES_OK : hip_fail(e);
   }
 
-  KernelFn fn = pick(split, a.num_blocks, has_d, has_o);
+  KernelFn fn = pick(kind, a.num_blocks, has_d, has_o);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;
   unsigned row_grid = unsigned(a.T);
-  if (!split && ATTNRES_ROW_WGS_PER_CU > 0) {
+  if (kind == Kind::kRow && ATTNRES_ROW_WGS_PER_CU > 0) {
     int dev = 0, cus = 0;
     e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

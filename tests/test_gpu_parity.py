@@ -38,7 +38,8 @@ def _paths(T, H=7168):
 
 def _path_of(name):
     from kimi_k3_attention_amd import attnres as A
-    return {"row": A.ATTNRES_PATH_ROW, "split": A.ATTNRES_PATH_SPLIT}[name]
+    return {"row": A.ATTNRES_PATH_ROW, "split": A.ATTNRES_PATH_SPLIT,
+            "any_h": A.ATTNRES_PATH_ANY_H}[name]
 
 
 def _run_and_check_all_paths(G, case, ref=None):
@@ -245,7 +246,7 @@ def test_cancelling_sources(G):
     assert np.isfinite(y_norm).all()
 
 
-@pytest.mark.parametrize("path_name", ["row", "split"])
+@pytest.mark.parametrize("path_name", ["row", "split", "any_h"])
 def test_bank_offsets_beyond_32_bits(G, path_name):
     """A bank whose element offsets exceed 2^31 (token stride 2^24 elements,
     about 4.8 GB): only the used rows are filled; sampled tokens are checked
@@ -327,7 +328,7 @@ def test_split_back_to_back_without_sync(G):
     assert A.attnres_device_status() == A.ATTNRES_OK
 
 
-@pytest.mark.parametrize("path_name", ["row", "split"])
+@pytest.mark.parametrize("path_name", ["row", "split", "any_h"])
 def test_graph_replay_matches_eager(G, path_name):
     """Calls captured in a hipGraph (torch.cuda.CUDAGraph) and replayed several
     times, with eager work and synchronisation in between, match the eager
