@@ -177,6 +177,41 @@ def test_interleaved_prefix_delta_and_out(G):
         assert (G.from_dev(d.bank) == ref.bank_after).all(), "bank after the call"
 
 
+@pytest.mark.parametrize("T,nb,onorm", [(64, 8, True), (200, 5, True), (3, 8, False)])
+def test_wide_dynamic_range(G, T, nb, onorm):
+    """Every bank, prefix and delta row scaled by its own power of two 2^k,
+    k uniform in [-40, 40] (exact in bf16): logits depend only on direction,
+    the mixture spans ~24 decades and the fp32 sums of squares stay in range.
+    All kernels against the fp64 oracle, eps as in the workloads."""
+    case = W.Case(f"range_T{T}_nb{nb}", T=T, nb=nb, has_onorm=onorm, widx=nb - 1,
+                  recipe="soft", seed=400 + T)
+    inp = W.make_inputs(case)
+    rng = np.random.default_rng(case.seed)
+    H, ts, ss = case.H, case.token_stride, case.slot_stride
+
+    def scale(bits, k):
+        # multiply bf16 values by 2^k by moving the exponent field (no value is
+        # zero or subnormal for these draws, and none leaves the normal range)
+        e = ((bits >> 7) & 0xFF).astype(np.int64) + k
+        assert (e > 0).all() and (e < 255).all()
+        return ((bits & 0x807F) | (e.astype(np.uint16) << 7)).astype(np.uint16)
+
+    for t in range(T):
+        inp.prefix[t] = scale(inp.prefix[t], int(rng.integers(-40, 41)))
+        if inp.delta is not None:
+            inp.delta[t] = scale(inp.delta[t], int(rng.integers(-40, 41)))
+        for i in range(nb):
+            o = t * ts + i * ss
+            inp.bank[o:o + H] = scale(inp.bank[o:o + H], int(rng.integers(-40, 41)))
+    ref = G.oracle_full(inp)
+    assert np.isfinite(ref.out_f64).all()
+    for path in _paths(T):
+        G.say(case.name, "path", path)
+        d = G.upload(inp)
+        G.run(d, path=path)
+        G.check_full(inp, G.download(d), ref)
+
+
 def test_soft_logits_mix(G):
     """O(1) logits so the mixture really mixes (the named workloads are nearly
     one-hot)."""
