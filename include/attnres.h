@@ -49,7 +49,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define ATTNRES_OK 0
 #define ATTNRES_E_NULL -1        /* a required pointer is NULL */
-#define ATTNRES_E_SHAPE -2       /* T < 0, H <= 0, max_blocks < 0, or sizes too large */
+#define ATTNRES_E_SHAPE -2       /* T < 0 or > 8388607, H <= 0, max_blocks < 0, or sizes too large */
 #define ATTNRES_E_UNSUPPORTED -3 /* H not a multiple of 8 or > ATTNRES_MAX_HIDDEN, or a forced
                                     path that cannot run these sizes */
 #define ATTNRES_E_NUM_BLOCKS -4  /* num_blocks < 0, > 8 or > max_blocks */
@@ -95,8 +95,9 @@ extern "C" {
  *   output_norm_eps    >= 0, finite (ignored without an output norm).
  *   block_write_idx    -1 = no bank write, else 0..max_blocks-1.
  *   out      [T, H] bf16, row stride H, device; must not overlap any input.
- *   T, H     tokens (>= 0; T == 0 is a no-op) and hidden size (a multiple of
- *            8, at most ATTNRES_MAX_HIDDEN).
+ *   T, H     tokens (0..8388607; T == 0 is a no-op: a dispatch counts its
+ *            lanes in 32 bits and a token takes at most 512) and hidden size
+ *            (a multiple of 8, at most ATTNRES_MAX_HIDDEN).
  *   stream   a hipStream_t (NULL = the default stream).
  *
  * All device pointers must be 16-byte aligned.  Asynchronous: returns after

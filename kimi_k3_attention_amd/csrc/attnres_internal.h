@@ -11,7 +11,9 @@ namespace attnres {
 constexpr int kHidden = 7168;          // the hidden size of the tuned row and split kernels
 constexpr int kMaxHidden = ATTNRES_MAX_HIDDEN;  // largest H of the any-H row kernel
 constexpr int kMaxBlocks = 8;          // bank rows a token may mix
-constexpr int64_t kMaxTokens = 2147483647LL;   // grid.x limit of the row path
+// A dispatch counts its lanes (workgroups x lanes per workgroup) in 32 bits;
+// every kernel uses at most 512 lanes per token.
+constexpr int64_t kMaxTokens = 4294967295LL / 512;  // 8,388,607
 constexpr int64_t kMaxStride = int64_t(1) << 46;
 
 // Row strides (prefix_stride, delta_stride, out_stride) are in elements and

@@ -90,6 +90,10 @@ CASES = [
     ("zero_H", dict(H=0), "ATTNRES_E_SHAPE"),
     ("negative_capacity", dict(cap=-1, nb=0), "ATTNRES_E_SHAPE"),
     ("too_many_tokens", dict(T=1 << 31), "ATTNRES_E_SHAPE"),
+    ("tokens_past_dispatch_limit", dict(T=8388608, H=8, ts=64, ss=8, blocks=0x80000000,
+                                        out=0x200000000), "ATTNRES_E_SHAPE"),
+    ("tokens_at_dispatch_limit", dict(T=8388607, H=8, ts=64, ss=8, blocks=0x80000000,
+                                      out=0x200000000), "ATTNRES_OK"),
     ("huge_stride", dict(ts=1 << 50), "ATTNRES_E_SHAPE"),
     ("valid_other_hidden_size", dict(H=4096), "ATTNRES_OK"),
     ("valid_smallest_hidden", dict(H=8), "ATTNRES_OK"),
