@@ -63,6 +63,44 @@ def test_single_token_decode(G, case):
     _run_and_check_all_paths(G, case)
 
 
+def test_benchmarked_configuration_replayed(G):
+    """The configuration the benchmark times: mid prefill (T=1024, 8 block
+    rows, delta, output norm, block_write_idx=3) over 4 resident input sets
+    with delta zeroed, calls captured in one hipGraph and replayed.  After the
+    first call each set is a fixed point (its bank slot 3 holds the prefix
+    row), so every replay must reproduce the oracle run on that state."""
+    from kimi_k3_attention_amd import attnres as A
+    base = W.mid_prefill()
+    devs, refs = [], []
+    for r in range(4):
+        case = W.with_(base, seed=base.seed + 100 * r)
+        inp = W.make_inputs(case)
+        inp.delta[:] = 0
+        # the state after one call: slot 3 = cur = prefix (delta is zero)
+        H, ts, ss = case.H, case.token_stride, case.slot_stride
+        bank = inp.bank.reshape(case.T, ts)
+        bank[:, case.widx * ss:case.widx * ss + H] = inp.prefix
+        refs.append((inp, G.oracle_full(inp)))
+        devs.append(G.upload(inp))
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(2):
+            for d in devs:
+                G.run(d)
+    for rep in range(3):
+        for d in devs:
+            d.out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, d in enumerate(devs):
+            inp, ref = refs[k]
+            G.say("benchmarked configuration, replay", rep, "set", k)
+            G.check_full(inp, G.download(d), ref)
+    assert A.attnres_device_status() == A.ATTNRES_OK
+
+
 def test_mid_prefill_full(G):
     case = W.mid_prefill()
     inp = W.make_inputs(case)
