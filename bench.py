@@ -260,6 +260,41 @@ def bench_hidden_sweep(Hs=HIDDEN_SWEEP, T: int = 1024, steps: int = 120):
     return res
 
 
+def bench_variant_sweep(T: int = 1024, windows: int = 4, steps: int = 120):
+    """T=1024 calls for every num_blocks 0..8 x delta x output norm (write slot
+    nb-1, or none at nb=0), each rotating over `windows` token windows of one
+    resident 4096-token input (footprint above the Infinity Cache)."""
+    case = W.Case("variant_sweep", T=T * windows, nb=8, widx=-1, seed=11)
+    s_all = Set(W.make_inputs(case))
+    H = case.H
+    res = {}
+    for nb in range(9):
+        for d in (False, True):
+            for o in (False, True):
+                widx = nb - 1 if nb > 0 else -1
+                c = W.Case("v", T=T, nb=nb, has_delta=d, has_onorm=o, widx=widx)
+                nbytes = c.algorithmic_bytes()
+
+                def call(w, nb=nb, d=d, o=o, widx=widx):
+                    sl = slice(w * T, (w + 1) * T)
+                    A.attnres_fwd(s_all.prefix[sl], s_all.delta[sl] if d else None,
+                                  s_all.bank3[sl], nb, s_all.res_w, s_all.rms_w, case.eps,
+                                  s_all.onw if o else None, case.oeps, widx, s_all.out[sl])
+
+                calls = [lambda w=w: call(w) for w in range(windows)]
+                for fn in calls:
+                    fn()
+                torch.cuda.synchronize()
+                t = time_graph(calls, steps, replays=3)
+                us = pct([x / steps * 1e3 for x in t], 50)
+                gbps = nbytes / us / 1e3
+                key = f"nb{nb}_d{int(d)}_o{int(o)}"
+                res[key] = dict(us=round(us, 2), GBps=round(gbps, 1),
+                                frac=round(gbps / HBM_PEAK_GBPS, 4))
+                log(f"variant {key}: {us:.2f} us, {gbps:.0f} GB/s")
+    return res
+
+
 CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
 CEILING_LIB = os.path.join(ROOT, "bench_ceiling.so")
 # (name, row reads, row writes to a separate buffer, row writes in place) per token
@@ -524,6 +559,8 @@ def main():
     ap.add_argument("--calibrate", action="store_true", help="run the known-size copy for counters")
     ap.add_argument("--hidden-sweep", action="store_true",
                     help="only the T=1024 mid-prefill recipe at other hidden sizes (any-H kernel)")
+    ap.add_argument("--variant-sweep", action="store_true",
+                    help="only T=1024 calls over num_blocks x delta x output norm")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output directories")
     ap.add_argument("--profile-commands", default=None, help="JSON of the commands that made them")
@@ -550,6 +587,16 @@ def main():
     A.attnres_init()
     if args.calibrate:
         calibration_copy()
+    if args.variant_sweep:
+        sweep = bench_variant_sweep()
+        print(json.dumps({"metric": "attention-residual forward throughput per variant",
+                          "unit": "GB/s", "higher_is_better": True, "data": "synthetic",
+                          "config": {"workload": "T=1024 tokens, H=7168, num_blocks 0..8 x delta "
+                                                 "x output norm, block_write_idx=nb-1, bf16",
+                                     "timing": "hipGraph replay"},
+                          "variants": sweep, "kernel_source_hash": kernel_source_hash()}),
+              flush=True)
+        return
     if args.hidden_sweep:
         sweep = bench_hidden_sweep()
         print(json.dumps({"metric": "attention-residual forward throughput at other hidden sizes",
