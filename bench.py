@@ -584,6 +584,10 @@ def main():
 
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+              "compute_units": props.multi_processor_count,
+              "memory_bytes": props.total_memory, "hip": getattr(torch.version, "hip", None),
+              "torch": torch.__version__}
     A.attnres_init()
     if args.calibrate:
         calibration_copy()
@@ -656,6 +660,7 @@ def main():
             "configs": ceiling}
     if cpu is not None:
         line["cpu_baseline"] = cpu
+    line["device"] = device
     line["kernel_source_hash"] = kernel_source_hash()
     print(json.dumps(line), flush=True)
 

@@ -63,6 +63,19 @@ def test_single_token_decode(G, case):
     _run_and_check_all_paths(G, case)
 
 
+@pytest.mark.parametrize("nb", [0, 1, 4, 8])
+def test_five_tokens_seed0(G, nb):
+    """The validation shape of the benchmark on the vLLM PR #54261 digest
+    ("Implementation breakdown" item 4 and the benchmark script under "Key
+    source snippets": 0, 1, 4 and 8 blocks on 5 tokens, seed 0), every
+    kernel, each flag combination."""
+    for d in (False, True):
+        for o in (False, True):
+            case = W.Case(f"five_nb{nb}_d{int(d)}_o{int(o)}", T=5, nb=nb, has_delta=d,
+                          has_onorm=o, widx=nb - 1 if nb else -1, seed=0)
+            _run_and_check_all_paths(G, case)
+
+
 def test_benchmarked_configuration_replayed(G):
     """The configuration the benchmark times: mid prefill (T=1024, 8 block
     rows, delta, output norm, block_write_idx=3) over 4 resident input sets
