@@ -277,6 +277,15 @@ def test_ragged_sizes(G, T, nb, widx):
     _run_and_check_all_paths(G, case)
 
 
+@pytest.mark.parametrize("T,nb,widx", [(2500, 1, 0), (1537, 0, -1), (4099, 1, -1)])
+def test_persistent_grid_few_blocks(G, T, nb, widx):
+    """Few source rows run a persistent grid (a few workgroups per CU, each
+    looping over tokens): token counts well above the grid, ragged against
+    it, every token checked."""
+    case = W.Case(f"persist_T{T}_nb{nb}", T=T, nb=nb, widx=widx, cap=2, seed=500 + T)
+    _run_and_check_all_paths(G, case)
+
+
 def test_slot_major_bank(G):
     case = W.Case("slot_major_T40_nb6", T=40, nb=6, widx=6, slot_major=True, seed=51)
     _run_and_check_all_paths(G, case)
