@@ -237,3 +237,26 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"(import\s+oracle|from\s+oracle|liboracle|oracle_attnres|oracle\.)",
                                      text), f"{f} uses the oracle"
+
+
+def test_plain_c_caller_builds_and_links():
+    """tests/c/abi_check, a C program that calls libattnres directly (no
+    Python), compiles against include/attnres.h and links the library, the
+    oracle and the HIP runtime; without a GPU it stops at the device query
+    with status 2."""
+    import importlib.util
+    import subprocess
+    spec = importlib.util.spec_from_file_location(
+        "build_abi_check", os.path.join(ROOT, "tests", "c", "build_abi_check.py"))
+    cbuild = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(cbuild)
+    exe = cbuild.build()
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except ImportError:
+        has_gpu = False
+    if has_gpu:
+        pytest.skip("a GPU is present: the run is covered by the GPU test")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2, res.stdout + res.stderr
