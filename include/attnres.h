@@ -98,7 +98,9 @@ extern "C" {
  *   T, H     tokens (0..8388607; T == 0 is a no-op: a dispatch counts its
  *            lanes in 32 bits and a token takes at most 512) and hidden size
  *            (a multiple of 8, at most ATTNRES_MAX_HIDDEN).
- *   stream   a hipStream_t (NULL = the default stream).
+ *   stream   a hipStream_t (NULL = the default stream of the current
+ *            device).  Kernels run on the stream's device, and the split
+ *            path uses that device's workspace, whichever device is current.
  *
  * All device pointers must be 16-byte aligned.  Asynchronous: returns after
  * enqueueing.  No allocation or host synchronisation happens once the split

@@ -934,16 +934,21 @@ int init_device_locked(int device) {
   return ATTNRES_OK;
 }
 
-// The current device's compute-unit count, cached per device.
-std::atomic<int> g_cus[kMaxDevices];
-int compute_units(int *cus) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+// The device a call's kernels run on: the stream's (the current device for
+// the null stream), whatever device is current.
+int launch_device(hipStream_t s, int *dev) {
+  hipError_t e = s ? hipStreamGetDevice(s, dev) : hipGetDevice(dev);
   if (e != hipSuccess) return hip_fail(e);
-  if (dev < 0 || dev >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
+  if (*dev < 0 || *dev >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
+  return ATTNRES_OK;
+}
+
+// A device's compute-unit count, cached per device.
+std::atomic<int> g_cus[kMaxDevices];
+int compute_units(int dev, int *cus) {
   int n = g_cus[dev].load(std::memory_order_relaxed);
   if (n <= 0) {
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e);
     if (n <= 0) n = 1;
     g_cus[dev].store(n, std::memory_order_relaxed);
@@ -998,15 +1003,14 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   kp.T = int(a.T);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  rc = launch_device(s, &dev);
+  if (rc != ATTNRES_OK) return rc;
   if (split) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e);
-    if (dev < 0 || dev >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
     std::lock_guard<std::mutex> lock(g_ws_mu);
     if (!g_ws[dev].base) {
       hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-      e = hipStreamIsCapturing(s, &st);
+      hipError_t e = hipStreamIsCapturing(s, &st);
       if (e != hipSuccess) return hip_fail(e);
       if (st != hipStreamCaptureStatusNone) return ATTNRES_E_NOT_INIT;
       rc = init_device_locked(dev);
@@ -1034,7 +1038,7 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   const int wpc = row_wgs_per_cu(a.num_blocks);
   if (kind == Kind::kRow && wpc > 0) {
     int cus = 0;
-    rc = compute_units(&cus);
+    rc = compute_units(dev, &cus);
     if (rc != ATTNRES_OK) return rc;
     const int64_t cap = int64_t(cus) * wpc;
     if (a.T > cap) row_grid = unsigned(cap);
