@@ -263,6 +263,34 @@ def test_wide_dynamic_range(G, T, nb, onorm):
         G.check_full(inp, G.download(d), ref)
 
 
+def _random_cases(n, seed):
+    """Seeded draws over the whole argument space the library accepts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        H = int(rng.choice([7168, 7168, 7168, 8 * int(rng.integers(1, 2049))]))
+        T = int(rng.choice([1, 2, 3, int(rng.integers(4, 40)), int(rng.integers(40, 300))]))
+        if H > 8192:
+            T = min(T, 64)
+        nb = int(rng.integers(0, 9))
+        cap = int(rng.integers(max(nb, 1), 9))
+        widx = int(rng.integers(-1, cap))
+        slot_major = bool(rng.random() < 0.2)
+        cases.append(W.Case(
+            f"rand{seed}_{k}_H{H}_T{T}_nb{nb}", T=T, nb=nb, cap=cap, H=H,
+            has_delta=bool(rng.random() < 0.6), has_onorm=bool(rng.random() < 0.6), widx=widx,
+            token_pad=0 if slot_major else 8 * int(rng.integers(0, 5)),
+            row_pad=8 * int(rng.choice([0, 0, int(rng.integers(1, 40))])),
+            slot_major=slot_major, recipe=str(rng.choice(["normal", "soft", "decode"])),
+            seed=10_000 + 100 * seed + k))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(40, 1) + _random_cases(80, 2), ids=lambda c: c.name)
+def test_random_configuration(G, case):
+    _run_and_check_all_paths(G, case)
+
+
 def test_soft_logits_mix(G):
     """O(1) logits so the mixture really mixes (the named workloads are nearly
     one-hot)."""
