@@ -64,8 +64,9 @@ extern "C" {
 #define ATTNRES_E_DEVICE_WAIT -13 /* a split-path cross-workgroup wait gave up (device flag) */
 
 /* ---- path selectors for attnres_fwd_path -------------------------------- */
-#define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: at H = 7168 split for T <= 16 (<= 32 with
-                                >= 2 blocks, <= 64 with >= 7 blocks), else row; other H: any-H */
+#define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: at H = 7168 split for T up to
+                                32/40/48/64/64/80/80/64/64 with 0..8 blocks, else row;
+                                other H: any-H */
 #define ATTNRES_PATH_ROW 1   /* one workgroup per token (the any-H kernel when H != 7168) */
 #define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (H = 7168, T <= 256) */
 #define ATTNRES_PATH_ANY_H 3 /* the any-H row kernel, also at H = 7168 */

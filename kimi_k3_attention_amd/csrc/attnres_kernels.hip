@@ -868,13 +868,13 @@ KernelFn pick_anyh(const AnyShape &sh, int nb, bool d, bool o) {
 
 enum class Kind { kRow, kSplit, kAnyH };
 
-// attnres_fwd's choice of kernel at H = 7168, from measured latency per call:
-// spreading a token over 14 CUs (split) beats one CU per token (row) while
-// the grid is small, the more so the more block rows a token has.
-Kind auto_kind(int64_t T, int nb) {
-  if (T <= 16 || (T <= 32 && nb >= 2) || (T <= 64 && nb >= 7)) return Kind::kSplit;
-  return Kind::kRow;
-}
+// attnres_fwd's choice of kernel at H = 7168, from measured latency per call
+// (graph replay, cold inputs, delta and output norm): spreading a token over
+// 14 CUs (split) beats one CU per token (row) up to this many tokens, by
+// block count.
+constexpr int kSplitMaxT[kMaxBlocks + 1] = {32, 40, 48, 64, 64, 80, 80, 64, 64};
+static_assert(80 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
+Kind auto_kind(int64_t T, int nb) { return T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow; }
 
 KernelFn pick(Kind kind, int nb, bool d, bool o) {
   switch (nb) {
