@@ -9,12 +9,14 @@
  *
  * Sources of the definition (the pages, cited by title and section):
  *  [ASC]  vllm-ascend PR #14840 "[Performance][Ops] Add Kimi K3 attention
- *         residual fusion", author's "Implementation walkthrough": per token,
- *         read the valid block residuals, append prefix_sum as the final
- *         candidate, RMS-normalise every candidate, score it with
- *         norm.weight * proj.weight, softmax across the valid candidates, form
- *         the weighted residual sum, cast back to the model dtype; capacity
- *         (shape[1]) is not the valid count, unused slots are never touched.
+ *         residual fusion", author's "Implementation walkthrough": for each
+ *         token the bank rows in use are taken, the current prefix sum joins
+ *         them as the last candidate, each candidate's RMS is normalised in
+ *         fp32 and scored against the product of the two weight vectors, the
+ *         scores become softmax weights over exactly those candidates, and
+ *         the weighted sum of the candidates is converted to the model's
+ *         dtype; the bank's slot dimension is its capacity, not the number
+ *         in use, and slots beyond that number take no part.
  *  [P1]   prhub digest of vLLM PR #54261 (native CUDA Kimi-K3 AttnRes made the
  *         default on SM100), "Implementation breakdown" items 1-3 and the
  *         kernel snippet under "Key source snippets": optional delta added
@@ -26,8 +28,8 @@
  *         breakdown" item 2: the fused query q_cache = rms_w * res_w.
  *
  * Readings taken where the pages are silent (each is applied once, here):
- *  R1 the softmax weights the RAW source rows (the "residual sum"); the
- *     normalised rows only produce the logits.
+ *  R1 the softmax weights the RAW source rows (the sum is over the residual
+ *     streams themselves); the normalised rows only produce the logits.
  *  R2 the current-layer source is cur = bf16_RNE(prefix + delta) (the row the
  *     kernel stores back), or prefix when there is no delta.
  *  R3 with a delta, prefix is overwritten with cur; without one it is left
