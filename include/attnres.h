@@ -107,7 +107,12 @@ extern "C" {
  * enqueueing.  No allocation or host synchronisation happens once the split
  * path's workspace exists (attnres_init, or the first uncaptured call that
  * needs it), so calls can be captured into a hipGraph.  Calls that use the
- * split path share one workspace per device and must be ordered on one stream.
+ * split path share one workspace per device and run one after another: when
+ * one comes on a different stream than the previous split call on that
+ * device, its stream first waits for the work enqueued on the previous stream
+ * (so that stream must still exist).  Inside graph capture no such wait is
+ * added: replays of graphs holding split calls must not overlap each other or
+ * other split calls on the device.
  */
 int attnres_fwd(void *prefix, const void *delta, void *blocks,
                 int64_t block_token_stride, int64_t block_slot_stride,

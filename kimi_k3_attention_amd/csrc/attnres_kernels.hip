@@ -896,10 +896,18 @@ constexpr size_t kPartBytes = size_t(ATTNRES_SPLIT_MAX_TOKENS) * kParts * kSlot 
 constexpr size_t kFlagBytes = 256;
 constexpr size_t kWorkspaceBytes = kPartBytes + kFlagBytes;
 
+// Split calls on one device must run one after another: they share the
+// workspace, and two split kernels running at once could each hold the
+// compute-unit slots the other's remaining parts need.  A split call on a
+// different stream than the previous one therefore makes its stream wait for
+// everything enqueued on the previous stream so far (outside graph capture).
 struct DeviceWorkspace {
   void *base = nullptr;
   uint64_t *part = nullptr;
   unsigned *flag = nullptr;
+  hipEvent_t handoff = nullptr;   // recorded on the previous stream at a switch
+  hipStream_t last_stream = nullptr;
+  bool has_last = false;
 };
 
 DeviceWorkspace g_ws[kMaxDevices];
@@ -918,9 +926,11 @@ int init_device_locked(int device) {
   if (e != hipSuccess) return hip_fail(e);
   if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e);
   void *base = nullptr;
+  hipEvent_t ev = nullptr;
   e = hipMalloc(&base, kWorkspaceBytes);
   if (e == hipSuccess) e = hipMemset(base, 0, kWorkspaceBytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
   if (e != hipSuccess) {
     if (base) (void)hipFree(base);
     (void)hipSetDevice(prev);
@@ -928,6 +938,7 @@ int init_device_locked(int device) {
   }
   DeviceWorkspace &w = g_ws[device];
   w.base = base;
+  w.handoff = ev;
   w.part = static_cast<uint64_t *>(base);
   w.flag = reinterpret_cast<unsigned *>(static_cast<char *>(base) + kPartBytes);
   (void)hipSetDevice(prev);
@@ -1008,16 +1019,27 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   if (rc != ATTNRES_OK) return rc;
   if (split) {
     std::lock_guard<std::mutex> lock(g_ws_mu);
-    if (!g_ws[dev].base) {
-      hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-      hipError_t e = hipStreamIsCapturing(s, &st);
-      if (e != hipSuccess) return hip_fail(e);
-      if (st != hipStreamCaptureStatusNone) return ATTNRES_E_NOT_INIT;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &st);
+    if (e != hipSuccess) return hip_fail(e);
+    const bool capturing = st != hipStreamCaptureStatusNone;
+    DeviceWorkspace &w = g_ws[dev];
+    if (!w.base) {
+      if (capturing) return ATTNRES_E_NOT_INIT;
       rc = init_device_locked(dev);
       if (rc != ATTNRES_OK) return rc;
     }
-    kp.ws_part = g_ws[dev].part;
-    kp.ws_flag = g_ws[dev].flag;
+    if (!capturing) {
+      if (w.has_last && w.last_stream != s) {
+        e = hipEventRecord(w.handoff, w.last_stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, w.handoff, 0);
+        if (e != hipSuccess) return hip_fail(e);
+      }
+      w.last_stream = s;
+      w.has_last = true;
+    }
+    kp.ws_part = w.part;
+    kp.ws_flag = w.flag;
   }
 
   const bool has_d = a.delta != nullptr, has_o = a.output_norm_weight != nullptr;
@@ -1141,6 +1163,7 @@ extern "C" void attnres_shutdown(void) {
       (void)hipSetDevice(d);
       (void)hipDeviceSynchronize();
       (void)hipFree(g_ws[d].base);
+      if (g_ws[d].handoff) (void)hipEventDestroy(g_ws[d].handoff);
       (void)hipSetDevice(prev);
       g_ws[d] = DeviceWorkspace{};
     }

@@ -451,6 +451,29 @@ def test_split_back_to_back_without_sync(G):
     assert A.attnres_device_status() == A.ATTNRES_OK
 
 
+def test_split_calls_on_several_streams(G):
+    """Split calls issued round-robin on three streams with no
+    synchronisation between the streams: the library orders them (a stream
+    switch waits for the previous stream's work), so every call sees its own
+    inputs and the shared workspace is never used twice at once."""
+    from kimi_k3_attention_amd import attnres as A
+    cases = [W.Case(f"streams{k}", T=5 + 3 * k, nb=6, widx=3, seed=600 + k) for k in range(6)]
+    inps = [W.make_inputs(c) for c in cases]
+    refs = [G.oracle_full(i) for i in inps]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for rep in range(5):
+        devs = [G.upload(i) for i in inps]
+        torch.cuda.synchronize()
+        for k, d in enumerate(devs):
+            with torch.cuda.stream(streams[k % 3]):
+                G.run(d, path=A.ATTNRES_PATH_SPLIT)
+        torch.cuda.synchronize()
+        for k, d in enumerate(devs):
+            G.say("several streams, repetition", rep, "call", k)
+            G.check_full(inps[k], G.download(d), refs[k])
+    assert A.attnres_device_status() == A.ATTNRES_OK
+
+
 @pytest.mark.parametrize("path_name", ["row", "split", "any_h"])
 def test_graph_replay_matches_eager(G, path_name):
     """Calls captured in a hipGraph (torch.cuda.CUDAGraph) and replayed several
