@@ -402,21 +402,41 @@ __device__ __forceinline__ float sum_sq(const float (&y)[SPL][8]) {
   return s;
 }
 
+// Combines a[0..N) pairwise into a[0] (a[j] with a[j + w] for w = 1, 2, 4,
+// ...): a fixed order with a dependency depth of ceil(log2 N).
+template <int N, typename Op>
+__device__ __forceinline__ float tree_reduce(float (&a)[N], Op op) {
+#pragma unroll
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int j = 0; j + w < N; j += 2 * w) a[j] = op(a[j], a[j + w]);
+  return a[0];
+}
+
 // Softmax over the NS sources.  Lane j (< NS) holds logit j; lane j of the
-// result holds p_j.  The normaliser is accumulated in online form (running
-// max m and running sum z of exp(l - m), rescaled whenever the max moves) on
-// wave-uniform values, identically in every wave.
+// result holds p_j.  Two passes: the maximum m of the logits (exact in any
+// order), then each lane's exp(l_j - m) and their sum z; both read the NS
+// lanes' values and combine them in a fixed pairwise order, so every wave
+// obtains the same values.  All logits exist at this point, so the running
+// rescale of an online softmax would only lengthen the dependency chain.
 template <int NS>
 __device__ __forceinline__ float softmax_lanes(float logit_lane) {
-  float m = lane_value(logit_lane, 0), z = 1.f;
+  if constexpr (NS == 1) {
+    // A single source: exp(l - l) / exp(l - l), i.e. 1, or NaN for a
+    // non-finite logit (l - l is not folded without fast-math).
+    return (logit_lane - logit_lane) + 1.f;
+  } else {
+    const int lane = threadIdx.x & (kWave - 1);
+    float a[NS];
 #pragma unroll
-  for (int j = 1; j < NS; ++j) {
-    const float l = lane_value(logit_lane, j);
-    const float mn = fmaxf(m, l);
-    z = z * __expf(m - mn) + __expf(l - mn);
-    m = mn;
+    for (int j = 0; j < NS; ++j) a[j] = lane_value(logit_lane, j);
+    const float m = tree_reduce(a, [](float x, float y) { return fmaxf(x, y); });
+    const float e = lane < NS ? __expf(logit_lane - m) : 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) a[j] = lane_value(e, j);
+    const float z = tree_reduce(a, [](float x, float y) { return x + y; });  // >= 1
+    return e * __builtin_amdgcn_rcpf(z);
   }
-  return __expf(logit_lane - m) * __builtin_amdgcn_rcpf(z);  // z >= 1
 }
 
 // ---------------------------------------------------------------------------
@@ -425,19 +445,24 @@ __device__ __forceinline__ float softmax_lanes(float logit_lane) {
 
 constexpr int kRowRows = kRowWaves * 4;  // 16-lane row partials per workgroup
 
+// Sums groups of four partials in a fixed order: four running sums (one per
+// float4 component, short dependency chains), then (x + y) + (z + w).
+__device__ __forceinline__ float sum_float4s(const float4 *v4, int n4) {
+  float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
+#pragma unroll
+  for (int i = 0; i < n4; ++i) {
+    const float4 a = v4[i];
+    sx += a.x;
+    sy += a.y;
+    sz += a.z;
+    sw += a.w;
+  }
+  return (sx + sy) + (sz + sw);
+}
+
 // Sums the kRowRows row partials of one value in a fixed order.
 __device__ __forceinline__ float sum_row_partials(const float *v) {
-  const float4 *v4 = reinterpret_cast<const float4 *>(v);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRowRows / 4; ++i) {
-    const float4 a = v4[i];
-    s += a.x;
-    s += a.y;
-    s += a.z;
-    s += a.w;
-  }
-  return s;
+  return sum_float4s(reinterpret_cast<const float4 *>(v), kRowRows / 4);
 }
 
 // The grid either has one workgroup per token or is persistent (a few
@@ -527,16 +552,7 @@ constexpr int kAnyMaxRows = kAnyMaxThreads / 16;  // 16-lane row partials per wo
 
 // Sums n4 groups of four row partials in a fixed order.
 __device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
-  const float4 *v4 = reinterpret_cast<const float4 *>(v);
-  float s = 0.f;
-  for (int i = 0; i < n4; ++i) {
-    const float4 a = v4[i];
-    s += a.x;
-    s += a.y;
-    s += a.z;
-    s += a.w;
-  }
-  return s;
+  return sum_float4s(reinterpret_cast<const float4 *>(v), n4);
 }
 
 // The row path's steps for a runtime row of p.nseg segments: blockDim.x lanes
@@ -663,10 +679,15 @@ __device__ __forceinline__ float gather(const uint64_t *tok_ws, int idx, uint32_
     }
     __builtin_amdgcn_s_sleep(ATTNRES_SPIN_SLEEP);
   }
-  float s = 0.f;
+  // Two interleaved running sums (even and odd parts), then their sum.
+  static_assert(kParts % 2 == 0, "parts are summed in pairs");
+  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int r = 0; r < kParts; ++r) s += value_of(w[r]);
-  return s;
+  for (int r = 0; r < kParts; r += 2) {
+    s0 += value_of(w[r]);
+    s1 += value_of(w[r + 1]);
+  }
+  return s0 + s1;
 }
 
 __device__ __forceinline__ float lane_shuffle(float v, int src) {
@@ -785,16 +806,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   tk.keep_packed();
   __syncthreads();
   if (lane < NV) {
-    const float4 *row = reinterpret_cast<const float4 *>(s_tr[lane]);
-    float v = 0.f;
-#pragma unroll
-    for (int i = 0; i < kWave / 4; ++i) {
-      const float4 a = row[i];
-      v += a.x;
-      v += a.y;
-      v += a.z;
-      v += a.w;
-    }
+    const float v = sum_float4s(reinterpret_cast<const float4 *>(s_tr[lane]), kWave / 4);
     tagged_store(slot + lane, v, gen);
   }
 
