@@ -177,6 +177,13 @@ def attnres_fwd(prefix: torch.Tensor, delta: Optional[torch.Tensor],
     dev = prefix.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU")
+    # The kernels dereference every pointer on prefix's device: a host tensor
+    # or one on another GPU would fault there, so it is refused here.
+    for name, t in (("delta", delta), ("blocks", blocks), ("res_w", res_w), ("rms_w", rms_w),
+                    ("output_norm_weight", output_norm_weight), ("out", out)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, prefix on {dev}: all tensors must be "
+                             "on the same GPU")
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         if not _dense(m):

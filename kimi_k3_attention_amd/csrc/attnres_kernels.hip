@@ -926,8 +926,12 @@ DeviceWorkspace g_ws[kMaxDevices];
 std::mutex g_ws_mu;
 std::atomic<int> g_last_hip{0};
 
+// Records a failed HIP call's error for attnres_last_hip_error and clears the
+// runtime's last-error state, so that the caller's next unrelated error check
+// does not report it again (the call has already returned ATTNRES_E_HIP).
 int hip_fail(hipError_t e) {
   g_last_hip.store(int(e));
+  (void)hipGetLastError();
   return ATTNRES_E_HIP;
 }
 
@@ -1029,8 +1033,12 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   int dev = 0;
   rc = launch_device(s, &dev);
   if (rc != ATTNRES_OK) return rc;
+  // A split call holds the workspace lock from the stream hand-off through
+  // its launch: another thread's split call on another stream may then only
+  // record its hand-off after this kernel is enqueued.
+  std::unique_lock<std::mutex> ws_lock;
   if (split) {
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+    ws_lock = std::unique_lock<std::mutex>(g_ws_mu);
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(s, &st);
     if (e != hipSuccess) return hip_fail(e);

@@ -474,6 +474,47 @@ def test_split_calls_on_several_streams(G):
     assert A.attnres_device_status() == A.ATTNRES_OK
 
 
+def test_split_calls_from_two_threads(G):
+    """Two host threads issue split calls at the same time, each on its own
+    stream (the library call runs without the GIL): the workspace hand-off
+    and the launch happen under one lock, so every result matches the
+    oracle."""
+    import threading
+    from kimi_k3_attention_amd import attnres as A
+    # Repeated calls must be idempotent: no delta, and the written slot (7) is
+    # not one of the 7 sources.
+    cases = [W.Case(f"threads{k}", T=3 + 2 * k, nb=7, widx=7, has_delta=False, seed=700 + k)
+             for k in range(8)]
+    inps = [W.make_inputs(c) for c in cases]
+    refs = [G.oracle_full(i) for i in inps]
+    devs = [G.upload(i) for i in inps]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(ks):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for _ in range(20):
+                    for k in ks:
+                        G.run(devs[k], path=A.ATTNRES_PATH_SPLIT)
+            stream.synchronize()
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(range(j, 8, 2),)) for j in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k, d in enumerate(devs):
+        G.say("two threads, call", k)
+        G.check_full(inps[k], G.download(d), refs[k])
+    assert A.attnres_device_status() == A.ATTNRES_OK
+
+
 @pytest.mark.parametrize("path_name", ["row", "split", "any_h"])
 def test_graph_replay_matches_eager(G, path_name):
     """Calls captured in a hipGraph (torch.cuda.CUDAGraph) and replayed several
@@ -523,6 +564,14 @@ def test_invalid_call_raises_and_touches_nothing(G):
         A.attnres_fwd(d.prefix, d.delta, d.bank3, 9, d.res_w, d.rms_w, case.eps, d.onw,
                       case.oeps, case.widx, d.out)
     assert e.value.name == "ATTNRES_E_NUM_BLOCKS"
+    # A host tensor among device tensors is refused by the binding before any
+    # library call (the kernels would dereference a host address).
+    for name in ("delta", "res_w", "out"):
+        args = dict(delta=d.delta, res_w=d.res_w, out=d.out)
+        args[name] = args[name].cpu()
+        with pytest.raises(ValueError, match=name):
+            A.attnres_fwd(d.prefix, args["delta"], d.bank3, case.nb, args["res_w"], d.rms_w,
+                          case.eps, d.onw, case.oeps, case.widx, args["out"])
     got = G.download(d)
     assert (got.prefix == inp.prefix).all() and (got.bank == inp.bank).all()
     assert (got.out == inp.out_init).all()
