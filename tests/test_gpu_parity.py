@@ -39,7 +39,18 @@ def _paths(T, H=7168):
 def _path_of(name):
     from kimi_k3_attention_amd import attnres as A
     return {"row": A.ATTNRES_PATH_ROW, "split": A.ATTNRES_PATH_SPLIT,
-            "any_h": A.ATTNRES_PATH_ANY_H}[name]
+            "any_h": A.ATTNRES_PATH_ANY_H, "any_h_large": A.ATTNRES_PATH_ANY_H}[name]
+
+
+# Rows over 8192 elements (four segments per lane, one workgroup per CU) at
+# token counts that fill the device several times over.
+LARGE_ROW_CASES = [
+    dict(H=16384, T=700, nb=8),
+    dict(H=12288, T=1100, nb=5, has_onorm=False),
+    dict(H=8200, T=600, nb=3, widx=-1),          # 1025 segments: halves of 513 and 512
+    dict(H=16376, T=530, nb=0),                  # masked halves, a single source
+    dict(H=10240, T=333, nb=7, has_delta=False),
+]
 
 
 def _run_and_check_all_paths(G, case, ref=None):
@@ -179,6 +190,36 @@ def test_other_hidden_sizes(G, kw):
     kw = dict(kw)
     case = W.other_hidden(kw.pop("H"), kw.pop("T"), kw.pop("nb"), **kw)
     _run_and_check_all_paths(G, case)
+
+
+@pytest.mark.parametrize("kw", LARGE_ROW_CASES, ids=lambda kw: f"H{kw['H']}_T{kw['T']}_nb{kw['nb']}")
+def test_large_rows_many_tokens(G, kw):
+    kw = dict(kw)
+    case = W.other_hidden(kw.pop("H"), kw.pop("T"), kw.pop("nb"), **kw)
+    _run_and_check_all_paths(G, case)
+
+
+def test_large_rows_back_to_back(G):
+    """Calls with 16384-element rows and very different token counts enqueued
+    back to back without synchronisation: every result matches the oracle."""
+    from kimi_k3_attention_amd import attnres as A
+    cases = [W.other_hidden(16384, T, nb, seed=900 + T) for T, nb in
+             ((900, 8), (3, 2), (520, 8), (1, 0), (777, 4), (260, 1))]
+    inps = [W.make_inputs(c) for c in cases]
+    refs = [G.oracle_full(i) for i in inps]
+    devs = [G.upload(i) for i in inps]
+    torch.cuda.synchronize()
+    for rep in range(2):
+        if rep:
+            devs = [G.upload(i) for i in inps]
+            torch.cuda.synchronize()
+        for d in devs:
+            G.run(d, path=A.ATTNRES_PATH_ANY_H)
+        torch.cuda.synchronize()
+        for k, d in enumerate(devs):
+            G.say("large rows back to back, repetition", rep, "call", k)
+            G.check_full(inps[k], G.download(d), refs[k])
+    assert A.attnres_device_status() == A.ATTNRES_OK
 
 
 def test_split_path_refuses_other_hidden_sizes(G):
@@ -515,7 +556,7 @@ def test_split_calls_from_two_threads(G):
     assert A.attnres_device_status() == A.ATTNRES_OK
 
 
-@pytest.mark.parametrize("path_name", ["row", "split", "any_h"])
+@pytest.mark.parametrize("path_name", ["row", "split", "any_h", "any_h_large"])
 def test_graph_replay_matches_eager(G, path_name):
     """Calls captured in a hipGraph (torch.cuda.CUDAGraph) and replayed several
     times, with eager work and synchronisation in between, match the eager
@@ -525,6 +566,8 @@ def test_graph_replay_matches_eager(G, path_name):
     path = _path_of(path_name)
     A.attnres_init()
     case = W.Case(f"graph_{path_name}", T=24, nb=6, widx=5, seed=70)
+    if path_name == "any_h_large":
+        case = W.other_hidden(16384, T=600, nb=6, seed=71)
     inp = W.make_inputs(case)
     inp.delta[:] = 0
     d = G.upload(inp)
