@@ -112,7 +112,11 @@ extern "C" {
  * device, its stream first waits for the work enqueued on the previous stream
  * (so that stream must still exist).  Inside graph capture no such wait is
  * added: replays of graphs holding split calls must not overlap each other or
- * other split calls on the device.
+ * other split calls on the device.  The ordering is per process: split calls
+ * of two processes running on one GPU at the same time can fill the compute
+ * units with waiting workgroups; the bounded wait then gives up and
+ * attnres_device_status reports ATTNRES_E_DEVICE_WAIT (the results of those
+ * calls are not valid).
  */
 int attnres_fwd(void *prefix, const void *delta, void *blocks,
                 int64_t block_token_stride, int64_t block_slot_stride,
