@@ -194,18 +194,24 @@ int oracle_attnres_fwd(int64_t T, int64_t H, uint16_t *prefix, const uint16_t *d
             l[j] = acc;
         }
 
-        /* Softmax over the nb+1 valid sources (max-shifted). */
-        double m = l[0];
-        for (int j = 1; j < nsrc; ++j)
-            if (l[j] > m)
-                m = l[j];
-        double z = 0.0;
-        for (int j = 0; j < nsrc; ++j) {
-            p[j] = exp(l[j] - m);
-            z += p[j];
+        /* Softmax over the nb+1 valid sources (max-shifted).  A single
+         * source has weight exactly 1 (R12), also when its logit is not a
+         * number (eps = 0 and an all-zero row make it 0/0). */
+        if (nsrc == 1) {
+            p[0] = 1.0;
+        } else {
+            double m = l[0];
+            for (int j = 1; j < nsrc; ++j)
+                if (l[j] > m)
+                    m = l[j];
+            double z = 0.0;
+            for (int j = 0; j < nsrc; ++j) {
+                p[j] = exp(l[j] - m);
+                z += p[j];
+            }
+            for (int j = 0; j < nsrc; ++j)
+                p[j] /= z;
         }
-        for (int j = 0; j < nsrc; ++j)
-            p[j] /= z;
 
         /* Weighted sum of the RAW source rows (R1). */
         for (int64_t h = 0; h < H; ++h) {

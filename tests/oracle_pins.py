@@ -186,6 +186,14 @@ def pin_nb0_is_normalised_current_residual(lib):
             torch.from_numpy(widen(cur)), (H,),
             torch.from_numpy(widen(w)), eps=1e-5).numpy()
         _close(r.out_f64, ref, 1e-13, "nb=0 with output norm vs torch rms_norm")
+    # A single source keeps weight 1 when its logit is 0/0 (eps = 0, an
+    # all-zero row): the output is that row, zero, and not a NaN.
+    zero = np.zeros((T, H), dtype=np.uint16)
+    r = O.attnres_oracle(zero, None, None, 0, 0, 0, 0, rw, rw, 0.0, None, 1e-6, -1, lib=lib)
+    assert np.all(r.probs == 1.0), "nb=0: weight 1 even for a 0/0 logit"
+    assert (r.out_bits == 0).all(), "nb=0, zero row, eps = 0: out is the zero row"
+    r = O.attnres_oracle(zero, None, None, 0, 0, 0, 0, rw, rw, 0.0, w, 1e-6, -1, lib=lib)
+    assert (widen(r.out_bits) == 0).all(), "nb=0 with output norm: a zero row stays zero"
 
 
 def _random_case(rng, T, H, nb, cap, scale_rows=True):
