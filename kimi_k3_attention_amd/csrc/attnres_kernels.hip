@@ -236,12 +236,13 @@ struct Token {
     bool ok[SPL];
 #pragma unroll
     for (int i = 0; i < SPL; ++i) ok[i] = in_row(p, seg0 + i * seg_step);
+    if constexpr (NB > 0)  // a single source needs no logit, hence no query
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      const int off = (seg0 + i * seg_step) * kSeg;
-      rms[i] = load_weight(p.rms_w + off, ok[i]);
-      res[i] = load_weight(p.res_w + off, ok[i]);
-    }
+      for (int i = 0; i < SPL; ++i) {
+        const int off = (seg0 + i * seg_step) * kSeg;
+        rms[i] = load_weight(p.rms_w + off, ok[i]);
+        res[i] = load_weight(p.res_w + off, ok[i]);
+      }
     const uint16_t *bank = p.blocks + t * p.tok_stride;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
@@ -348,6 +349,18 @@ struct Token {
           y[i][2 * k + 1] = fmaf(pj, bf_hi(x[j][i][k]), y[i][2 * k + 1]);
         }
     }
+  }
+
+  // y = cur in fp32 (exact): the mixture when cur is the only source, whose
+  // softmax weight is exactly 1.
+  __device__ __forceinline__ void cur_as_mix(float (&y)[SPL][8]) const {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y[i][2 * k] = bf_lo(x[NB][i][k]);
+        y[i][2 * k + 1] = bf_hi(x[NB][i][k]);
+      }
   }
 
   // The in-place writes of cur (prefix with a delta, bank slot widx).  By the
@@ -498,6 +511,23 @@ attnres_row_kernel(KParams p) {
   for (int64_t t = blockIdx.x; t < p.T; t += t_step, par ^= 1) {
     Token<NB, DELTA, ONORM, SPL> tk;
     tk.issue(p, t, seg0, seg_step);
+    if constexpr (NB == 0) {
+      // One source, weight exactly 1: y = cur, no logit, and the output
+      // norm's sum of squares is cur's (one reduction, none without a norm).
+      tk.finish_cur();
+      tk.issue_onw(p, seg0, seg_step);
+      float y[SPL][8];
+      tk.cur_as_mix(y);
+      float rsig = 1.f;
+      if constexpr (ONORM) {
+        const float sy = row16_sum(sum_sq<SPL>(y));
+        if (row_leader) s_ysq[par][rowslot] = sy;
+        __syncthreads();
+        rsig = rsqrtf(sum_row_partials(s_ysq[par]) * kInvHidden + p.out_eps);
+      }
+      tk.store(p, t, seg0, seg_step, y, rsig);
+      continue;
+    }
     u32x4 qh[SPL], ql[SPL];
     tk.query(qh, ql);
     tk.finish_cur();
@@ -579,6 +609,22 @@ attnres_anyh_kernel(KParams p) {
 
   Token<NB, DELTA, ONORM, SPL, MASKED> tk;
   tk.issue(p, t, seg0, seg_step);
+  if constexpr (NB == 0) {
+    // One source, weight exactly 1 (as in the row kernel).
+    tk.finish_cur();
+    tk.issue_onw(p, seg0, seg_step);
+    float y[SPL][8];
+    tk.cur_as_mix(y);
+    float rsig = 1.f;
+    if constexpr (ONORM) {
+      const float sy = row16_sum(sum_sq<SPL>(y));
+      if (row_leader) s_ysq[rowslot] = sy;
+      __syncthreads();
+      rsig = rsqrtf(sum_row_partials_n(s_ysq, n4) * p.inv_h + p.out_eps);
+    }
+    tk.store(p, t, seg0, seg_step, y, rsig);
+    return;
+  }
   u32x4 qh[SPL], ql[SPL];
   tk.query(qh, ql);
   tk.finish_cur();
@@ -769,6 +815,31 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   uint64_t *const tok_ws = p.ws_part + size_t(t) * kParts * kSlot;
   uint64_t *const slot = tok_ws + part * kSlot;
 
+  if constexpr (NB == 0) {
+    // One source, weight exactly 1: y = cur.  Only an output norm needs the
+    // token's sum of squares; the parts exchange it through word 0 alone
+    // (so every such call still rewrites word 0 of all parts).  Without a
+    // norm nothing is exchanged.
+    uint32_t gen0 = 0;
+    if constexpr (ONORM) gen0 = tag_of(tagged_load(slot)) + 1u;
+    Token<NB, DELTA, ONORM, 1> tk;
+    tk.issue(p, t, part * kPartThreads + lane, 0);
+    tk.finish_cur();
+    tk.issue_onw(p, part * kPartThreads + lane, 0);
+    float y[1][8];
+    tk.cur_as_mix(y);
+    float rsig = 1.f;
+    if constexpr (ONORM) {
+      const float s = wave_sum_lane63(sum_sq<1>(y));
+      if (lane == kWave - 1) tagged_store(slot, s, gen0);
+      float total = 0.f;
+      if (lane == 0) total = gather(tok_ws, 0, gen0, p.ws_flag);
+      rsig = rsqrtf(lane_value(total, 0) * kInvHidden + p.out_eps);
+    }
+    tk.store(p, t, part * kPartThreads + lane, 0, y, rsig);
+    return;
+  }
+
   // This call's generation (issued first; used only when publishing).
   const uint32_t gen = tag_of(tagged_load(slot)) + 1u;
 
@@ -883,8 +954,9 @@ enum class Kind { kRow, kSplit, kAnyH };
 // attnres_fwd's choice of kernel at H = 7168, from measured latency per call
 // (graph replay, cold inputs, delta and output norm): spreading a token over
 // 14 CUs (split) beats one CU per token (row) up to this many tokens, by
-// block count.
-constexpr int kSplitMaxT[kMaxBlocks + 1] = {32, 40, 48, 64, 64, 80, 80, 64, 64};
+// block count.  A single source (nb = 0) needs no exchange on the row path,
+// which is then faster at every T.
+constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 48, 64, 64, 80, 80, 64, 64};
 static_assert(80 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
 Kind auto_kind(int64_t T, int nb) { return T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow; }
 

@@ -53,8 +53,9 @@ LARGE_ROW_CASES = [
 ]
 
 
-def _run_and_check_all_paths(G, case, ref=None):
-    inp = W.make_inputs(case)
+def _run_and_check_all_paths(G, case, ref=None, inp=None):
+    if inp is None:
+        inp = W.make_inputs(case)
     if ref is None:
         ref = G.oracle_full(inp)
     for path in _paths(case.T, case.H):
@@ -353,6 +354,19 @@ def test_persistent_grid_few_blocks(G, T, nb, widx):
     it, every token checked."""
     case = W.Case(f"persist_T{T}_nb{nb}", T=T, nb=nb, widx=widx, cap=2, seed=500 + T)
     _run_and_check_all_paths(G, case)
+
+
+@pytest.mark.parametrize("T,has_onorm", [(4, False), (4, True), (40, True), (300, False)])
+def test_single_source_zero_row_eps0(G, T, has_onorm):
+    """nb = 0 with eps = 0 and an all-zero current row: the logit is 0/0, the
+    single source still has weight 1, so out is the zero row (finite) on
+    every path, as in the oracle."""
+    case = W.Case(f"zero_row_T{T}", T=T, nb=0, has_delta=False, has_onorm=has_onorm, eps=0.0,
+                  seed=40 + T)
+    inp = W.make_inputs(case)
+    inp.prefix[1] = 0
+    inp.prefix[T - 1] = 0
+    _run_and_check_all_paths(G, case, inp=inp)
 
 
 def test_slot_major_bank(G):
