@@ -62,6 +62,9 @@
 #ifndef ATTNRES_NT_STORE_CUR
 #define ATTNRES_NT_STORE_CUR ATTNRES_NT_STORES  // policy for the in-place prefix / bank rows
 #endif
+#ifndef ATTNRES_SPLIT_DPP_WORDS
+#define ATTNRES_SPLIT_DPP_WORDS 8       // split path: words summed by DPP instead of via LDS
+#endif
 #ifndef ATTNRES_EARLY_CUR_STORE
 #define ATTNRES_EARLY_CUR_STORE 0       // write prefix / bank rows as soon as cur exists
 #endif
@@ -850,8 +853,40 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   tk.finish_cur();
   if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, part * kPartThreads + lane, 0);
 
-  // Per-lane values, transposed through LDS so that lane v sums value v over
-  // the wave, then published with one store of tagged words.
+  // Per-lane values summed over the wave, then published with one store of
+  // tagged words (lane v holds word v).  A few words are summed with DPP
+  // wave reductions (independent chains); more are transposed through LDS so
+  // that lane v sums value v over the wave.
+  if constexpr (NV <= ATTNRES_SPLIT_DPP_WORDS) {
+    float ss[NS], dq[NS], val[NV];
+    tk.partials(qh, ql, ss, dq);
+    if constexpr (ONORM) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        val[pair_row_start(NS, j)] = ss[j];
+#pragma unroll
+        for (int k = j + 1; k < NS; ++k) {
+          float g = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) g = dot2(tk.x[j][0][w], tk.x[k][0][w], g);
+          val[pair_row_start(NS, j) + (k - j)] = g;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) val[j] = ss[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) val[Words::kDot + j] = dq[j];
+    float word = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const float sum = lane_value(wave_sum_lane63(val[v]), kWave - 1);
+      word = lane == v ? sum : word;
+    }
+    tk.keep_packed();
+    if (lane < NV) tagged_store(slot + lane, word, gen);
+  } else {
   {
     float ss[NS], dq[NS];
     tk.partials(qh, ql, ss, dq);
@@ -879,6 +914,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   if (lane < NV) {
     const float v = sum_float4s(reinterpret_cast<const float4 *>(s_tr[lane]), kWave / 4);
     tagged_store(slot + lane, v, gen);
+  }
   }
 
   tk.issue_onw(p, part * kPartThreads + lane, 0);
