@@ -79,17 +79,18 @@ class Set:
         if self.delta is not None:
             self.delta.zero_()  # repeated in-place calls stay a fixed point
 
-    def call(self, nb=None, token=None, path=None):
+    def call(self, nb=None, token=None, path=None, ntok=1):
+        """The whole set, or the ntok tokens from `token` on."""
         c = self.case
         nb = c.nb if nb is None else nb
         if token is None:
             A.attnres_fwd(self.prefix, self.delta, self.bank3, nb, self.res_w, self.rms_w, c.eps,
                           self.onw, c.oeps, c.widx, self.out, path=path)
         else:
-            sl = slice(token, token + 1)
+            sl = slice(token, token + ntok)
             A.attnres_fwd(self.prefix[sl], None if self.delta is None else self.delta[sl],
                           self.bank3[sl], nb, self.res_w, self.rms_w, c.eps, self.onw, c.oeps,
-                          c.widx, self.out[sl])
+                          c.widx, self.out[sl], path=path)
 
 
 def time_graph(calls, steps: int, replays: int = 1):
@@ -192,6 +193,36 @@ def bench_decode(steps: int):
                               bytes=W.Case("x", T=1, nb=nb).algorithmic_bytes())
         log(f"decode nb={nb}: cold {res[f'nb{nb}']['cold_us']:.2f} us, warm {res[f'nb{nb}']['warm_us']:.2f} us")
     return res
+
+
+LATENCY_TOKENS = (1, 8, 16, 24, 32, 40, 48, 56, 64, 80, 96, 128)
+
+
+def bench_latency_grid(n: int = 4096):
+    """Small batches: us per call of T tokens through the row kernel and the
+    split kernel (both forced), num_blocks 0..8, delta and output norm on.
+    Consecutive calls take consecutive T-token windows of one resident
+    4096-token input (decode recipe, ~650 MB, above the Infinity Cache), so
+    every call reads cold rows; hipGraph replay of at least 512 calls."""
+    case = W.Case("latency_grid", T=n, nb=8, recipe="decode", seed=1)
+    s = Set(W.make_inputs(case))
+    grid = {}
+    for T in LATENCY_TOKENS:
+        windows = n // T
+        steps = max(windows, 512)
+        row = {}
+        for nb in range(9):
+            cell = {}
+            for name, path in (("row", A.ATTNRES_PATH_ROW), ("split", A.ATTNRES_PATH_SPLIT)):
+                calls = [lambda w=w, nb=nb, path=path: s.call(nb=nb, token=w * T, path=path, ntok=T)
+                         for w in range(windows)]
+                t = time_graph(calls, steps, replays=3)
+                cell[name] = round(pct([x / steps * 1e3 for x in t], 50), 3)
+            row[f"nb{nb}"] = cell
+        grid[f"T{T}"] = row
+        log(f"latency grid T={T}: " + " ".join(
+            f"nb{k}:{row[f'nb{k}']['row']:.2f}/{row[f'nb{k}']['split']:.2f}" for k in range(9)))
+    return grid
 
 
 def bench_long(steps: int = 20):
@@ -559,6 +590,8 @@ def main():
     ap.add_argument("--calibrate", action="store_true", help="run the known-size copy for counters")
     ap.add_argument("--hidden-sweep", action="store_true",
                     help="only the T=1024 mid-prefill recipe at other hidden sizes (any-H kernel)")
+    ap.add_argument("--latency-grid", action="store_true",
+                    help="small batches: row vs split kernel over T and num_blocks")
     ap.add_argument("--variant-sweep", action="store_true",
                     help="only T=1024 calls over num_blocks x delta x output norm")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -600,6 +633,16 @@ def main():
                                      "timing": "hipGraph replay"},
                           "variants": sweep, "kernel_source_hash": kernel_source_hash()}),
               flush=True)
+        return
+    if args.latency_grid:
+        grid = bench_latency_grid()
+        print(json.dumps({"metric": "attention-residual forward latency, small batches",
+                          "unit": "us/call", "higher_is_better": False, "data": "synthetic",
+                          "config": {"workload": "T tokens (cold rows), H=7168, num_blocks 0..8, "
+                                                 "delta and output norm on, no bank write, bf16; "
+                                                 "row and split kernels forced",
+                                     "timing": "hipGraph replay"},
+                          "grid": grid, "kernel_source_hash": kernel_source_hash()}), flush=True)
         return
     if args.hidden_sweep:
         sweep = bench_hidden_sweep()
