@@ -461,8 +461,27 @@ __device__ __forceinline__ float softmax_lanes(float logit_lane) {
 
 constexpr int kRowRows = kRowWaves * 4;  // 16-lane row partials per workgroup
 
-// Sums groups of four partials in a fixed order: four running sums (one per
-// float4 component, short dependency chains), then (x + y) + (z + w).
+// Sums N groups of four partials (LDS) in a fixed order: every read is issued
+// before the first add (one LDS round trip, not one per few reads), then four
+// running sums, one per float4 component, and (x + y) + (z + w).
+template <int N>
+__device__ __forceinline__ float sum_float4s(const float4 *v4) {
+  float4 a[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = v4[i];
+  __builtin_amdgcn_sched_barrier(0);
+  float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    sx += a[i].x;
+    sy += a[i].y;
+    sz += a[i].z;
+    sw += a[i].w;
+  }
+  return (sx + sy) + (sz + sw);
+}
+
+// The same sum for a runtime number of groups.
 __device__ __forceinline__ float sum_float4s(const float4 *v4, int n4) {
   float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
 #pragma unroll
@@ -478,7 +497,7 @@ __device__ __forceinline__ float sum_float4s(const float4 *v4, int n4) {
 
 // Sums the kRowRows row partials of one value in a fixed order.
 __device__ __forceinline__ float sum_row_partials(const float *v) {
-  return sum_float4s(reinterpret_cast<const float4 *>(v), kRowRows / 4);
+  return sum_float4s<kRowRows / 4>(reinterpret_cast<const float4 *>(v));
 }
 
 // The grid either has one workgroup per token or is persistent (a few
@@ -912,7 +931,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   tk.keep_packed();
   __syncthreads();
   if (lane < NV) {
-    const float v = sum_float4s(reinterpret_cast<const float4 *>(s_tr[lane]), kWave / 4);
+    const float v = sum_float4s<kWave / 4>(reinterpret_cast<const float4 *>(s_tr[lane]));
     tagged_store(slot + lane, v, gen);
   }
   }
