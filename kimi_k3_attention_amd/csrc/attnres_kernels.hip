@@ -17,12 +17,15 @@
 //  * Row path (H = 7168, many tokens): one 448-lane workgroup (7 waves, two
 //    segments per lane) per token.  Per-lane fp32 sum-of-squares and query
 //    dot of every source (packed bf16 dot products), a 16-lane DPP reduction,
-//    a cross-row reduction through LDS, logits, the softmax normaliser in
-//    online form, the fp32 mixture, the optional output RMSNorm (a second LDS
-//    reduction), bf16 round-to-nearest-even stores.
+//    a cross-row reduction through LDS, logits, the softmax (maximum, then
+//    the sum of exponentials, over at most 9 lanes), the fp32 mixture, the
+//    optional output RMSNorm (a second LDS reduction), bf16
+//    round-to-nearest-even stores.  With no bank rows the only source has
+//    weight 1: no logit, and at most the output norm's reduction.
 //  * Split path (H = 7168, few tokens): 14 single-wave workgroups per token,
 //    each owning 512 elements of every row, so one token is spread over 14
-//    CUs.  Per-part sums (and, with an output norm, the sources' Gram matrix)
+//    CUs.  Per-part sums (and, with an output norm, the sources' Gram matrix),
+//    summed over the wave by DPP (few words) or an LDS transposition (many),
 //    are exchanged once through a device workspace of self-validating tagged
 //    words read and written with agent-scope atomics (the 8 XCDs do not share
 //    L2); no reset is needed between calls or graph replays.  Waits are
