@@ -484,19 +484,6 @@ __device__ __forceinline__ float sum_float4s(const float4 *v4) {
   return (sx + sy) + (sz + sw);
 }
 
-// The same sum for a runtime number of groups.
-__device__ __forceinline__ float sum_float4s(const float4 *v4, int n4) {
-  float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
-#pragma unroll
-  for (int i = 0; i < n4; ++i) {
-    const float4 a = v4[i];
-    sx += a.x;
-    sy += a.y;
-    sz += a.z;
-    sw += a.w;
-  }
-  return (sx + sy) + (sz + sw);
-}
 
 // Sums the kRowRows row partials of one value in a fixed order.
 __device__ __forceinline__ float sum_row_partials(const float *v) {
@@ -605,9 +592,28 @@ attnres_row_kernel(KParams p) {
 constexpr int kAnyMaxThreads = 512;               // 8 waves
 constexpr int kAnyMaxRows = kAnyMaxThreads / 16;  // 16-lane row partials per workgroup
 
-// Sums n4 groups of four row partials in a fixed order.
+// Sums the first n4 (<= kAnyMaxRows / 4) groups of four row partials in a
+// fixed order.  All kAnyMaxRows / 4 groups of the row are read at once (the
+// row always holds that many, so the reads stay in bounds) and the groups
+// past n4 count as zero.
 __device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
-  return sum_float4s(reinterpret_cast<const float4 *>(v), n4);
+  constexpr int kMax4 = kAnyMaxRows / 4;
+  const float4 *v4 = reinterpret_cast<const float4 *>(v);
+  float4 a[kMax4];
+#pragma unroll
+  for (int i = 0; i < kMax4; ++i) a[i] = v4[i];
+  __builtin_amdgcn_sched_barrier(0);
+  float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMax4; ++i) {
+    if (i < n4) {
+      sx += a[i].x;
+      sy += a[i].y;
+      sz += a[i].z;
+      sw += a[i].w;
+    }
+  }
+  return (sx + sy) + (sz + sw);
 }
 
 // The row path's steps for a runtime row of p.nseg segments: blockDim.x lanes
