@@ -20,6 +20,9 @@
  *     if delta:               prefix[t] = cur                     (in place)
  *     if block_write_idx>=0:  blocks[t, block_write_idx] = cur    (in place)
  *
+ * With num_blocks == 0 the only source, cur, has weight exactly 1 (y = cur),
+ * also when its logit is not a number (rms_eps = 0 and an all-zero row).
+ *
  * All reads see the state before the call (a written slot that is also a
  * source contributes its old value).  Bank slots num_blocks..max_blocks-1 are
  * never read, and nothing but out, prefix (with a delta) and the one bank row
