@@ -38,7 +38,9 @@ from kimi_k3_attention_amd import workloads as W  # noqa: E402
 METRIC = "AttnRes µs/call (T=1, 0/4/8 blk) + achieved HBM GB/s at T=1024, 8 blk, H=7168"
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
-DOMINANT_KERNEL = "attnres_row_kernel<8, true, true>"
+# The mid-prefill call's kernel: 8 block rows, delta, output norm, and the
+# two rewritten rows read through the cache (T >= 1024, written slot 3 < 8).
+DOMINANT_KERNEL = "attnres_row_kernel<8, true, true, true>"
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "attnres_row_kernel_mid_prefill_T1024_traffic.json")
 CALIBRATION_BYTES = 512 << 20
@@ -328,8 +330,14 @@ def bench_variant_sweep(T: int = 1024, windows: int = 4, steps: int = 120):
 
 CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
 CEILING_LIB = os.path.join(ROOT, "bench_ceiling.so")
-# (name, row reads, row writes to a separate buffer, row writes in place) per token
-CEILING_CONFIGS = (("mid_prefill_10r_1w_2inplace", 10, 1, 2), ("10r_3w", 10, 3, 0),
+# The mid-prefill call's own buffers and row roles (ceiling_mid): 8 bank rows,
+# prefix and delta read; out, prefix and bank slot 3 written; the two
+# rewritten rows read through the cache (as the library's row kernel does for
+# this call) or streamed.
+CEILING_MID_CONFIGS = (("mid_prefill_cached", 1), ("mid_prefill_streamed", 0))
+# (name, row reads, row writes to a separate buffer, row writes in place) per
+# token, every row of a token in one buffer, every row streamed.
+CEILING_CONFIGS = (("one_buffer_10r_1w_2inplace", 10, 1, 2), ("10r_3w", 10, 3, 0),
                    ("long_prefill_9r_1w", 9, 1, 0), ("read_only_10r", 10, 0, 0),
                    ("copy_1r_1w", 1, 1, 0))
 
@@ -356,6 +364,8 @@ def load_ceiling_probe():
     lib = ctypes.CDLL(CEILING_LIB)
     vp, i64, ci, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
     lib.ceiling_stream.argtypes = [vp, i64, vp, i64, ci, ci, ci, i64, u32, vp]
+    lib.ceiling_mid.argtypes = [vp, vp, vp, vp, i64, ci, vp]
+    lib.ceiling_mid.restype = ci
     lib.ceiling_stream.restype = ci
     return lib
 
@@ -368,6 +378,35 @@ def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168):
     bytes), so the token count differs between configurations."""
     lib = load_ceiling_probe()
     res = {}
+    T = round(call_bytes / (2 * H * 13))
+    for name, cached in CEILING_MID_CONFIGS:
+        per_set = 2 * H * T * 11  # bank 8 rows + prefix + delta + out
+        sets = []
+        for _ in range(max(2, -(-2 * MALL_BYTES // per_set))):
+            bank = torch.randint(-30000, 30000, (T * 8 * H,), dtype=torch.int16, device="cuda")
+            pf = torch.randint(-30000, 30000, (T * H,), dtype=torch.int16, device="cuda")
+            dl = torch.randint(-30000, 30000, (T * H,), dtype=torch.int16, device="cuda")
+            out = torch.empty(T * H, dtype=torch.int16, device="cuda")
+            sets.append((bank, pf, dl, out))
+
+        def call_mid(st, cached=cached, name=name):
+            rc = lib.ceiling_mid(st[0].data_ptr(), st[1].data_ptr(), st[2].data_ptr(),
+                                 st[3].data_ptr(), T, cached, torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"ceiling probe {name} failed ({rc})")
+
+        calls = [lambda st=st: call_mid(st) for st in sets]
+        for fn in calls:
+            fn()
+        torch.cuda.synchronize()
+        t = time_graph(calls, steps, replays=3)
+        us = pct([x / steps * 1e3 for x in t], 50)
+        nbytes = 2 * H * T * 13
+        res[name] = dict(T=T, us=round(us, 2), GBps=round(nbytes / us / 1e3, 1),
+                         frac=round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4))
+        log(f"ceiling probe {name}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
+        del sets
+        torch.cuda.empty_cache()
     for name, reads, wd, wi in CEILING_CONFIGS:
         T = max(1, round(call_bytes / (2 * H * (reads + wd + wi))))
         footprint = 2 * H * T * (reads + wd)
@@ -558,7 +597,7 @@ def summarize_profile(trace_dir, fetch_dir, write_dir, commands):
     res = {}
     for tag, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         pk = per_kernel(_csv_rows(d, "counter_collection.csv"))
-        ours = [v for (n, g), vals in pk.items() if "attnres_row_kernel<8, true, true>" in n for v in vals]
+        ours = [v for (n, g), vals in pk.items() if DOMINANT_KERNEL in n for v in vals]
         # the calibration copy: the kernel whose counter reads about the copy size
         calib = [(n, g, float(np.median(v))) for (n, g), v in pk.items()
                  if "attnres" not in n and len(v) >= 3]
@@ -694,10 +733,11 @@ def main():
     if longp is not None:
         line["long_prefill"] = longp
     if ceiling is not None:
-        probe = ceiling["mid_prefill_10r_1w_2inplace"]
+        probe = ceiling["mid_prefill_cached"]
         line["traffic_ceiling"] = {
-            "probe": "same bytes and launch shape as the mid-prefill call (10 row reads, 1 row "
-                     "write, 2 in-place row writes per token), no arithmetic",
+            "probe": "the mid-prefill call's buffers, row roles, launch shape and cache policy "
+                     "(8 bank rows, prefix and delta read, the 2 rewritten rows through the "
+                     "cache; out, prefix and bank slot 3 written), no arithmetic",
             "GBps": probe["GBps"],
             "kernel_fraction": None if mid is None else round(mid["gbps"] / probe["GBps"], 4),
             "configs": ceiling}

@@ -90,6 +90,8 @@ constexpr int kPartThreads = kSegs / kParts;  // 64 = one wave
 constexpr int kSlot = 64;                     // 64-bit words per (token, part) workspace slot
 constexpr int kSlotYsq = kSlot - 1;           // where a part's sum of y^2 goes
 constexpr int kSpinLimit = 1 << 20;           // bounded cross-workgroup wait
+// Fourth word of a raw buffer resource: 32-bit data format, no swizzle.
+constexpr int kBufferFormat = 0x00020000;
 constexpr float kInvHidden = 1.0f / kHidden;
 
 // Row path grid.  With few source rows a token moves little data, and with
@@ -217,7 +219,7 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 // MASKED (rows whose length is not a multiple of the workgroup's reach):
 // a segment at or past p.nseg loads nothing and holds zeros, which add
 // nothing to any sum, and is never stored.
-template <int NB, bool DELTA, bool ONORM, int SPL, bool MASKED = false>
+template <int NB, bool DELTA, bool ONORM, int SPL, bool MASKED = false, bool CACHE_RW = false>
 struct Token {
   static constexpr int NS = NB + 1;
   u32x4 rms[SPL], res[SPL], onw[SPL];  // weights
@@ -231,6 +233,21 @@ struct Token {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     if (!MASKED) return load_stream(q);
     return ok ? load_stream(q) : zero;
+  }
+  // With CACHE_RW, the two rows a call also writes (prefix with a delta, and
+  // the bank slot widx when it is a source) are read through the cache at
+  // normal priority, so that their writes find the lines resident, while rows
+  // only read stream past the cache (load_row).  The slot is chosen at run
+  // time, so its load sits in a uniform branch beside the streaming one; it
+  // is a buffer load, a different instruction, which the compiler cannot
+  // merge with the streaming load (merging two plain loads would drop the
+  // non-temporal hint).  The record size is the row, so a segment past a
+  // masked row's end reads zero, as load_row's masking gives.
+  __device__ __forceinline__ static u32x4 load_rewritten(const KParams &p, const uint16_t *row,
+                                                         int seg) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(row), 0, p.nseg * kSeg * int(sizeof(uint16_t)), kBufferFormat);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, seg * kSeg * int(sizeof(uint16_t)), 0, 0);
   }
   __device__ __forceinline__ static u32x4 load_weight(const uint16_t *q, bool ok) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -250,14 +267,33 @@ struct Token {
         res[i] = load_weight(p.res_w + off, ok[i]);
       }
     const uint16_t *bank = p.blocks + t * p.tok_stride;
+    const uint16_t *prow = p.prefix + t * p.prefix_stride;
+    if constexpr (CACHE_RW) {
+      // Both in-place rows (prefix, and the written slot, a source here) are
+      // read through the cache; the slot is chosen at run time.
+      static_assert(DELTA && NB > 0, "two rewritten rows need a delta and a source slot");
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NB; ++j) {
+        const uint16_t *row = bank + j * p.slot_stride;
+        if (j == p.widx) {
 #pragma unroll
-      for (int i = 0; i < SPL; ++i)
-        x[j][i] = load_row(bank + j * p.slot_stride + (seg0 + i * seg_step) * kSeg, ok[i]);
+          for (int i = 0; i < SPL; ++i) x[j][i] = load_rewritten(p, row, seg0 + i * seg_step);
+        } else {
 #pragma unroll
-    for (int i = 0; i < SPL; ++i)
-      x[NB][i] = load_row(p.prefix + t * p.prefix_stride + (seg0 + i * seg_step) * kSeg, ok[i]);
+          for (int i = 0; i < SPL; ++i) x[j][i] = load_row(row + (seg0 + i * seg_step) * kSeg, ok[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) x[NB][i] = load_rewritten(p, prow, seg0 + i * seg_step);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+          x[j][i] = load_row(bank + j * p.slot_stride + (seg0 + i * seg_step) * kSeg, ok[i]);
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(prow + (seg0 + i * seg_step) * kSeg, ok[i]);
+    }
     if constexpr (DELTA)
 #pragma unroll
       for (int i = 0; i < SPL; ++i)
@@ -493,7 +529,7 @@ __device__ __forceinline__ float sum_row_partials(const float *v) {
 // The grid either has one workgroup per token or is persistent (a few
 // workgroups per CU looping over tokens); LDS partials are double-buffered by
 // iteration parity so one barrier per phase suffices.
-template <int NB, bool DELTA, bool ONORM>
+template <int NB, bool DELTA, bool ONORM, bool CACHE_RW = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kRowThreads, kRowThreads),
                                // the unified arch+acc register file counts double
                                amdgpu_num_vgpr(ATTNRES_ROW_MAX_VGPRS / 2)))
@@ -521,7 +557,7 @@ attnres_row_kernel(KParams p) {
   const int seg0 = int(threadIdx.x);
   const int seg_step = kRowThreads;
   for (int64_t t = blockIdx.x; t < p.T; t += t_step, par ^= 1) {
-    Token<NB, DELTA, ONORM, SPL> tk;
+    Token<NB, DELTA, ONORM, SPL, false, CACHE_RW> tk;
     tk.issue(p, t, seg0, seg_step);
     if constexpr (NB == 0) {
       // One source, weight exactly 1: y = cur, no logit, and the output
@@ -977,7 +1013,10 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
 using KernelFn = void (*)(KParams);
 
 template <int NB>
-KernelFn row_fn(bool d, bool o) {
+KernelFn row_fn(bool d, bool o, bool cache_rw) {
+  if constexpr (NB > 0)
+    if (d && cache_rw)
+      return o ? attnres_row_kernel<NB, true, true, true> : attnres_row_kernel<NB, true, false, true>;
   if (d) return o ? attnres_row_kernel<NB, true, true> : attnres_row_kernel<NB, true, false>;
   return o ? attnres_row_kernel<NB, false, true> : attnres_row_kernel<NB, false, false>;
 }
@@ -1015,6 +1054,10 @@ KernelFn pick_anyh(const AnyShape &sh, int nb, bool d, bool o) {
 
 enum class Kind { kRow, kSplit, kAnyH };
 
+// Fewest tokens for which the row kernel reads the two rewritten rows through
+// the cache (measured crossover between 512 and 1024 tokens at nb = 1, 4, 8).
+constexpr int64_t kCacheRewrittenMinT = 1024;
+
 // attnres_fwd's choice of kernel at H = 7168, from measured latency per call
 // (graph replay, cold inputs, delta and output norm): spreading a token over
 // 14 CUs (split) beats one CU per token (row) up to this many tokens, by
@@ -1024,10 +1067,10 @@ constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 48, 64, 64, 80, 80, 64, 64};
 static_assert(80 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
 Kind auto_kind(int64_t T, int nb) { return T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow; }
 
-KernelFn pick(Kind kind, int nb, bool d, bool o) {
+KernelFn pick(Kind kind, int nb, bool d, bool o, bool cache_rw) {
   switch (nb) {
 #define ATTNRES_CASE(N) \
-  case N: return kind == Kind::kSplit ? split_fn<N>(d, o) : row_fn<N>(d, o);
+  case N: return kind == Kind::kSplit ? split_fn<N>(d, o) : row_fn<N>(d, o, cache_rw);
     ATTNRES_CASE(0) ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
     ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
 #undef ATTNRES_CASE
@@ -1210,7 +1253,14 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
     return e == hipSuccess ? ATTNRES_OK : hip_fail(e);
   }
 
-  KernelFn fn = pick(kind, a.num_blocks, has_d, has_o);
+  // Reading the two rows a call also writes (prefix with a delta, and a
+  // written slot that is a source) through the cache pays once a call
+  // streams many tokens: T = 1024, nb = 8: 33.7 -> 32.6 us, T = 4096:
+  // 131 -> 117 us.  Below about 1024 tokens (latency-bound), or with one
+  // such row, streaming reads are faster.
+  const bool cache_rw = kind == Kind::kRow && has_d && a.block_write_idx >= 0 &&
+                        a.block_write_idx < a.num_blocks && a.T >= kCacheRewrittenMinT;
+  KernelFn fn = pick(kind, a.num_blocks, has_d, has_o, cache_rw);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;
   unsigned row_grid = unsigned(a.T);
   const int wpc = row_wgs_per_cu(a.num_blocks);

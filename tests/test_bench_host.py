@@ -27,7 +27,7 @@ def _counter_run(directory, ours_kib, copy_kib):
     """A counter_collection.csv as rocprofv3 writes it: three dispatches of the
     dominant kernel and three of the calibration copy, plus an unrelated small
     kernel."""
-    ours = "void attnres::(anonymous namespace)::attnres_row_kernel<8, true, true>(attnres::KParams)"
+    ours = f"void attnres::(anonymous namespace)::{bench.DOMINANT_KERNEL}(attnres::KParams)"
     copy = "void at::native::vectorized_elementwise_kernel<4, copy>(...)"
     other = "void at::native::fill_kernel(...)"
     rows = []
@@ -55,7 +55,7 @@ def test_traffic_is_scaled_by_the_calibration_copy(tmp_path, profiles_dir):
     _counter_run(tmp_path / "write", [30000.0, 30500.0, 29000.0], copy_kib)
     _write_csv(str(tmp_path / "trace" / "a" / "mid_kernel_stats.csv"),
                ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
-               [["attnres_row_kernel<8, true, true>", 10, 33600.0, 33000.0, 34000.0, 99.9]])
+               [[bench.DOMINANT_KERNEL, 10, 33600.0, 33000.0, 34000.0, 99.9]])
     bench.summarize_profile(str(tmp_path / "trace"), str(tmp_path / "fetch"),
                             str(tmp_path / "write"), {"trace": "cmd"})
     t = json.load(open(profiles_dir / "traffic.json"))

@@ -61,3 +61,38 @@ def test_probe_rejects_unknown_shapes():
     import bench
     lib = bench.load_ceiling_probe()
     assert lib.ceiling_stream(None, 0, None, 0, 7, 1, 0, 4, 0, None) == -1
+    assert lib.ceiling_mid(None, None, None, None, 4, 1, None) == -1
+
+
+@pytest.mark.parametrize("cached", [0, 1])
+def test_mid_probe_moves_every_row(cached):
+    """The mid-prefill-layout probe reads all 8 bank rows, prefix and delta,
+    and writes out, prefix and bank slot 3 (nothing else), whichever cache
+    policy its two rewritten rows are read with."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bench
+    lib = bench.load_ceiling_probe()
+    T = 6
+    rng = np.random.default_rng(40 + cached)
+    bank_h = rng.integers(0, 1 << 16, size=T * 8 * H, dtype=np.uint16)
+    pf_h = rng.integers(0, 1 << 16, size=T * H, dtype=np.uint16)
+    dl_h = rng.integers(0, 1 << 16, size=T * H, dtype=np.uint16)
+    out_h = np.full(T * H, 0x7F85, dtype=np.uint16)
+    dev = [torch.from_numpy(a.view(np.int16)).cuda() for a in (bank_h, pf_h, dl_h, out_h)]
+    rc = lib.ceiling_mid(dev[0].data_ptr(), dev[1].data_ptr(), dev[2].data_ptr(), dev[3].data_ptr(),
+                         T, cached, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    bank, pf, dl, out = (d.cpu().numpy().view(np.uint16) for d in dev)
+    b = bank_h.reshape(T, 8, H).view(np.uint32).reshape(T, 8, H // 2)
+    p32 = pf_h.view(np.uint32).reshape(T, H // 2)
+    d32 = dl_h.view(np.uint32).reshape(T, H // 2)
+    cur = p32 ^ d32
+    want_out = np.bitwise_xor.reduce(b, axis=1) ^ p32 ^ d32
+    want_bank = b.copy()
+    want_bank[:, 3] = cur
+    assert (out.view(np.uint32).reshape(T, H // 2) == want_out).all()
+    assert (pf.view(np.uint32).reshape(T, H // 2) == cur).all()
+    assert (bank.view(np.uint32).reshape(T, 8, H // 2) == want_bank).all()
+    assert (dl == dl_h).all()

@@ -369,6 +369,25 @@ def test_single_source_zero_row_eps0(G, T, has_onorm):
     _run_and_check_all_paths(G, case, inp=inp)
 
 
+# Calls of at least 1024 tokens whose written slot is also a source, with a
+# delta: the row kernel then reads prefix and that slot through the cache.
+CACHED_REWRITE_CASES = [
+    dict(T=1024, nb=8, widx=0, slot_major=True),
+    dict(T=1100, nb=5, widx=4, token_pad=64, row_pad=16),
+    dict(T=1536, nb=2, widx=1, has_onorm=False),
+    dict(T=4099, nb=1, widx=0),
+    dict(T=2048, nb=7, widx=3, cap=7),
+]
+
+
+@pytest.mark.parametrize("kw", CACHED_REWRITE_CASES,
+                         ids=lambda kw: f"T{kw['T']}_nb{kw['nb']}_w{kw['widx']}")
+def test_cached_rewritten_rows(G, kw):
+    kw = dict(kw)
+    case = W.Case(f"cached_rw_T{kw['T']}", seed=60 + kw["T"] % 97, **kw)
+    _run_and_check_all_paths(G, case)
+
+
 def test_slot_major_bank(G):
     case = W.Case("slot_major_T40_nb6", T=40, nb=6, widx=6, slot_major=True, seed=51)
     _run_and_check_all_paths(G, case)
