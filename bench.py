@@ -739,7 +739,9 @@ def main():
                      "(8 bank rows, prefix and delta read, the 2 rewritten rows through the "
                      "cache; out, prefix and bank slot 3 written), no arithmetic",
             "GBps": probe["GBps"],
-            "kernel_fraction": None if mid is None else round(mid["gbps"] / probe["GBps"], 4),
+            # both medians over their graph replays
+            "kernel_fraction": None if mid is None else round(
+                mid["bytes"] / mid["us"]["p50"] / 1e3 / probe["GBps"], 4),
             "configs": ceiling}
     if cpu is not None:
         line["cpu_baseline"] = cpu

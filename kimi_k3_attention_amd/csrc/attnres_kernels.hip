@@ -229,6 +229,22 @@ struct Token {
   __device__ __forceinline__ static bool in_row(const KParams &p, int seg) {
     return !MASKED || seg < p.nseg;
   }
+  // Byte offset of a lane's segment i within a row.  Past segment 0 it
+  // exceeds the 4 KB immediate offset of a load or store, and the compiler
+  // would then form a 64-bit address for every row (and keep the stores'
+  // live through the kernel); held opaque in one 32-bit register, it is
+  // shared by all rows, each addressed as scalar row base + this offset.
+  __device__ __forceinline__ static uint32_t seg_bytes(int seg0, int seg_step, int i) {
+    uint32_t b = uint32_t(seg0 + i * seg_step) * uint32_t(kSeg * sizeof(uint16_t));
+    if (i > 0) asm("" : "+v"(b));
+    return b;
+  }
+  __device__ __forceinline__ static const uint16_t *at(const uint16_t *row, uint32_t b) {
+    return reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(row) + b);
+  }
+  __device__ __forceinline__ static uint16_t *at(uint16_t *row, uint32_t b) {
+    return reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(row) + b);
+  }
   __device__ __forceinline__ static u32x4 load_row(const uint16_t *q, bool ok) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     if (!MASKED) return load_stream(q);
@@ -244,10 +260,10 @@ struct Token {
   // non-temporal hint).  The record size is the row, so a segment past a
   // masked row's end reads zero, as load_row's masking gives.
   __device__ __forceinline__ static u32x4 load_rewritten(const KParams &p, const uint16_t *row,
-                                                         int seg) {
+                                                         uint32_t bytes) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(row), 0, p.nseg * kSeg * int(sizeof(uint16_t)), kBufferFormat);
-    return __builtin_amdgcn_raw_buffer_load_b128(r, seg * kSeg * int(sizeof(uint16_t)), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(bytes), 0, 0);
   }
   __device__ __forceinline__ static u32x4 load_weight(const uint16_t *q, bool ok) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -257,14 +273,17 @@ struct Token {
 
   __device__ __forceinline__ void issue(const KParams &p, int64_t t, int seg0, int seg_step) {
     bool ok[SPL];
+    uint32_t sb[SPL];
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) ok[i] = in_row(p, seg0 + i * seg_step);
+    for (int i = 0; i < SPL; ++i) {
+      ok[i] = in_row(p, seg0 + i * seg_step);
+      sb[i] = seg_bytes(seg0, seg_step, i);
+    }
     if constexpr (NB > 0)  // a single source needs no logit, hence no query
 #pragma unroll
       for (int i = 0; i < SPL; ++i) {
-        const int off = (seg0 + i * seg_step) * kSeg;
-        rms[i] = load_weight(p.rms_w + off, ok[i]);
-        res[i] = load_weight(p.res_w + off, ok[i]);
+        rms[i] = load_weight(at(p.rms_w, sb[i]), ok[i]);
+        res[i] = load_weight(at(p.res_w, sb[i]), ok[i]);
       }
     const uint16_t *bank = p.blocks + t * p.tok_stride;
     const uint16_t *prow = p.prefix + t * p.prefix_stride;
@@ -277,27 +296,27 @@ struct Token {
         const uint16_t *row = bank + j * p.slot_stride;
         if (j == p.widx) {
 #pragma unroll
-          for (int i = 0; i < SPL; ++i) x[j][i] = load_rewritten(p, row, seg0 + i * seg_step);
+          for (int i = 0; i < SPL; ++i) x[j][i] = load_rewritten(p, row, sb[i]);
         } else {
 #pragma unroll
-          for (int i = 0; i < SPL; ++i) x[j][i] = load_row(row + (seg0 + i * seg_step) * kSeg, ok[i]);
+          for (int i = 0; i < SPL; ++i) x[j][i] = load_row(at(row, sb[i]), ok[i]);
         }
       }
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) x[NB][i] = load_rewritten(p, prow, seg0 + i * seg_step);
+      for (int i = 0; i < SPL; ++i) x[NB][i] = load_rewritten(p, prow, sb[i]);
     } else {
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-          x[j][i] = load_row(bank + j * p.slot_stride + (seg0 + i * seg_step) * kSeg, ok[i]);
+          x[j][i] = load_row(at(bank + j * p.slot_stride, sb[i]), ok[i]);
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(prow + (seg0 + i * seg_step) * kSeg, ok[i]);
+      for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(at(prow, sb[i]), ok[i]);
     }
     if constexpr (DELTA)
 #pragma unroll
       for (int i = 0; i < SPL; ++i)
-        d[i] = load_row(p.delta + t * p.delta_stride + (seg0 + i * seg_step) * kSeg, ok[i]);
+        d[i] = load_row(at(p.delta + t * p.delta_stride, sb[i]), ok[i]);
     // Keep the scheduler from sinking any of these loads below the arithmetic.
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -309,8 +328,7 @@ struct Token {
     if constexpr (ONORM)
 #pragma unroll
       for (int i = 0; i < SPL; ++i) {
-        const int seg = seg0 + i * seg_step;
-        onw[i] = load_weight(p.onw + seg * kSeg, in_row(p, seg));
+        onw[i] = load_weight(at(p.onw, seg_bytes(seg0, seg_step, i)), in_row(p, seg0 + i * seg_step));
       }
   }
 
@@ -328,6 +346,7 @@ struct Token {
         qh[i][k] = pack_bf16x2(a, b);
         ql[i][k] = pack_bf16x2(a - bf_lo(qh[i][k]), b - bf_hi(qh[i][k]));
       }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // cur = bf16_RNE(prefix + delta) into x[NB].  The fp32 sum of two bf16
@@ -415,12 +434,12 @@ struct Token {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
       if (!in_row(p, seg0 + i * seg_step)) continue;
-      const int64_t off = int64_t(seg0 + i * seg_step) * kSeg;
+      const uint32_t b = seg_bytes(seg0, seg_step, i);
       if constexpr (DELTA)
-        store_stream<ATTNRES_NT_STORE_CUR>(p.prefix + t * p.prefix_stride + off, x[NB][i]);
+        store_stream<ATTNRES_NT_STORE_CUR>(at(p.prefix + t * p.prefix_stride, b), x[NB][i]);
       if (p.widx >= 0)
         store_stream<ATTNRES_NT_STORE_CUR>(
-            p.blocks + t * p.tok_stride + p.widx * p.slot_stride + off, x[NB][i]);
+            at(p.blocks + t * p.tok_stride + p.widx * p.slot_stride, b), x[NB][i]);
     }
   }
 
@@ -431,7 +450,6 @@ struct Token {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
       if (!in_row(p, seg0 + i * seg_step)) continue;
-      const int64_t off = int64_t(seg0 + i * seg_step) * kSeg;
       u32x4 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -441,7 +459,7 @@ struct Token {
         else
           o[k] = pack_bf16x2(y[i][2 * k], y[i][2 * k + 1]);
       }
-      store_stream(p.out + t * p.out_stride + off, o);
+      store_stream(at(p.out + t * p.out_stride, seg_bytes(seg0, seg_step, i)), o);
     }
     if (!ATTNRES_EARLY_CUR_STORE) store_cur(p, t, seg0, seg_step);
   }
@@ -656,7 +674,7 @@ __device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
 // (whole waves, at most kAnyMaxThreads) with SPL segments each, blockDim.x *
 // SPL >= p.nseg.  With two segments per lane a token fits 128 VGPRs (four
 // waves per SIMD); four segments may take 256.
-template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM>
+template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWave, kAnyMaxThreads),
                                amdgpu_waves_per_eu(SPL <= 2 ? 4 : 2)))
 attnres_anyh_kernel(KParams p) {
@@ -674,7 +692,7 @@ attnres_anyh_kernel(KParams p) {
   const int seg0 = int(threadIdx.x);  // whole-line loads, as in the row kernel
   const int seg_step = nthreads;
 
-  Token<NB, DELTA, ONORM, SPL, MASKED> tk;
+  Token<NB, DELTA, ONORM, SPL, MASKED, CACHE_RW> tk;
   tk.issue(p, t, seg0, seg_step);
   if constexpr (NB == 0) {
     // One source, weight exactly 1 (as in the row kernel).
@@ -1027,7 +1045,11 @@ KernelFn split_fn(bool d, bool o) {
 }
 
 template <int SPL, bool MASKED, int NB>
-KernelFn anyh_fn(bool d, bool o) {
+KernelFn anyh_fn(bool d, bool o, bool cache_rw) {
+  if constexpr (NB > 0)
+    if (d && cache_rw)
+      return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, true>
+               : attnres_anyh_kernel<SPL, MASKED, NB, true, false, true>;
   if (d)
     return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true>
              : attnres_anyh_kernel<SPL, MASKED, NB, true, false>;
@@ -1036,15 +1058,16 @@ KernelFn anyh_fn(bool d, bool o) {
 }
 
 template <int NB>
-KernelFn anyh_pick(const AnyShape &sh, bool d, bool o) {
-  if (sh.spl == 2) return sh.masked ? anyh_fn<2, true, NB>(d, o) : anyh_fn<2, false, NB>(d, o);
-  return sh.masked ? anyh_fn<4, true, NB>(d, o) : anyh_fn<4, false, NB>(d, o);
+KernelFn anyh_pick(const AnyShape &sh, bool d, bool o, bool c) {
+  if (sh.spl == 2)
+    return sh.masked ? anyh_fn<2, true, NB>(d, o, c) : anyh_fn<2, false, NB>(d, o, c);
+  return sh.masked ? anyh_fn<4, true, NB>(d, o, c) : anyh_fn<4, false, NB>(d, o, c);
 }
 
-KernelFn pick_anyh(const AnyShape &sh, int nb, bool d, bool o) {
+KernelFn pick_anyh(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw) {
   switch (nb) {
 #define ATTNRES_CASE(N) \
-  case N: return anyh_pick<N>(sh, d, o);
+  case N: return anyh_pick<N>(sh, d, o, cache_rw);
     ATTNRES_CASE(0) ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
     ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
 #undef ATTNRES_CASE
@@ -1054,9 +1077,19 @@ KernelFn pick_anyh(const AnyShape &sh, int nb, bool d, bool o) {
 
 enum class Kind { kRow, kSplit, kAnyH };
 
-// Fewest tokens for which the row kernel reads the two rewritten rows through
-// the cache (measured crossover between 512 and 1024 tokens at nb = 1, 4, 8).
-constexpr int64_t kCacheRewrittenMinT = 1024;
+// Smallest call, in elements per row array (T * H), for which the row
+// kernels read the two rewritten rows through the cache.  Measured crossover:
+// between 512 and 1024 tokens at H = 7168 (nb = 1, 4, 8), and for the any-H
+// kernel between about 4 and 8 million elements from H = 2048 to 16384.
+constexpr int64_t kCacheRewrittenMinElems = int64_t(1024) * 7168;
+
+// Whether a row-kernel call reads its two rewritten rows through the cache:
+// it has a delta (prefix is rewritten), writes a slot that is also a source,
+// and is large enough.
+bool cache_rewritten(const FwdArgs &a) {
+  return a.delta != nullptr && a.block_write_idx >= 0 && a.block_write_idx < a.num_blocks &&
+         a.T * a.H >= kCacheRewrittenMinElems;
+}
 
 // attnres_fwd's choice of kernel at H = 7168, from measured latency per call
 // (graph replay, cold inputs, delta and output norm): spreading a token over
@@ -1245,7 +1278,7 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   hipError_t e;
   if (any_h) {
     const AnyShape sh = anyh_shape(a.H);
-    KernelFn fn = pick_anyh(sh, a.num_blocks, has_d, has_o);
+    KernelFn fn = pick_anyh(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
     if (!fn) return ATTNRES_E_NUM_BLOCKS;
     void *args[] = {&kp};
     e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(unsigned(a.T)),
@@ -1258,8 +1291,7 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   // streams many tokens: T = 1024, nb = 8: 33.7 -> 32.6 us, T = 4096:
   // 131 -> 117 us.  Below about 1024 tokens (latency-bound), or with one
   // such row, streaming reads are faster.
-  const bool cache_rw = kind == Kind::kRow && has_d && a.block_write_idx >= 0 &&
-                        a.block_write_idx < a.num_blocks && a.T >= kCacheRewrittenMinT;
+  const bool cache_rw = kind == Kind::kRow && cache_rewritten(a);
   KernelFn fn = pick(kind, a.num_blocks, has_d, has_o, cache_rw);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;
   unsigned row_grid = unsigned(a.T);

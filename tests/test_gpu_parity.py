@@ -377,11 +377,16 @@ CACHED_REWRITE_CASES = [
     dict(T=1536, nb=2, widx=1, has_onorm=False),
     dict(T=4099, nb=1, widx=0),
     dict(T=2048, nb=7, widx=3, cap=7),
+    # the any-H kernel's cached variant (T * H at or above 1024 * 7168)
+    dict(H=8192, T=1024, nb=8, widx=3),
+    dict(H=2880, T=2560, nb=4, widx=2),                       # masked rows
+    dict(H=16376, T=449, nb=2, widx=1, has_onorm=False),      # four segments per lane, masked
+    dict(H=12288, T=600, nb=6, widx=5, token_pad=64),
 ]
 
 
 @pytest.mark.parametrize("kw", CACHED_REWRITE_CASES,
-                         ids=lambda kw: f"T{kw['T']}_nb{kw['nb']}_w{kw['widx']}")
+                         ids=lambda kw: f"H{kw.get('H', 7168)}_T{kw['T']}_nb{kw['nb']}_w{kw['widx']}")
 def test_cached_rewritten_rows(G, kw):
     kw = dict(kw)
     case = W.Case(f"cached_rw_T{kw['T']}", seed=60 + kw["T"] % 97, **kw)

@@ -1,0 +1,57 @@
+"""Register use of the built kernels, read on the CPU from the gfx950 code
+object inside libattnres.so: no kernel spills registers to scratch memory,
+and the row kernel fits the 128 VGPRs that let two 448-lane workgroups share
+a compute unit.  A spill costs a stream of scratch traffic per lane beside
+the row traffic the kernels are built around."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from kimi_k3_attention_amd import build as kbuild
+
+LLVM = "/opt/rocm/llvm/bin"
+
+
+def _kernels(tmp_path):
+    objdump, readelf = os.path.join(LLVM, "llvm-objdump"), os.path.join(LLVM, "llvm-readelf")
+    if not (os.path.exists(objdump) and os.path.exists(readelf)):
+        pytest.skip("ROCm LLVM tools not installed")
+    if not os.path.exists(kbuild.LIB):
+        kbuild.build()
+    lib = tmp_path / "libattnres.so"
+    shutil.copy(kbuild.LIB, lib)
+    # Writes each offloaded code object next to the copy.
+    subprocess.run([objdump, "--offloading", str(lib)], check=True, capture_output=True)
+    objs = [p for p in tmp_path.iterdir() if "gfx950" in p.name]
+    assert len(objs) == 1, [p.name for p in tmp_path.iterdir()]
+    notes = subprocess.run([readelf, "--notes", str(objs[0])], check=True, capture_output=True,
+                           text=True).stdout
+    kernels = {}
+    for block in re.split(r"\n\s+- \.agpr_count", notes)[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        if name.endswith(".kd"):
+            continue
+
+        def field(key):
+            m = re.search(rf"\.{key}:\s+(\d+)", block)
+            return int(m.group(1)) if m else None
+        kernels[name] = dict(vgprs=field("vgpr_count"), spills=field("vgpr_spill_count"),
+                             scratch=field("private_segment_fixed_size"))
+    assert kernels, "no kernel metadata found"
+    return kernels
+
+
+def test_no_kernel_spills_to_scratch(tmp_path):
+    ks = _kernels(tmp_path)
+    bad = {n: k for n, k in ks.items() if k["scratch"] or k["spills"]}
+    assert not bad, bad
+
+
+def test_row_kernel_fits_two_workgroups_per_cu(tmp_path):
+    ks = _kernels(tmp_path)
+    row = {n: k for n, k in ks.items() if "attnres_row_kernel" in n}
+    assert len(row) == 9 * 4 + 8 * 2  # nb 0..8 x (delta, norm); cached variants at nb >= 1
+    assert all(k["vgprs"] <= 128 for k in row.values()), row
