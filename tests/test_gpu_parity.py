@@ -333,6 +333,35 @@ def test_random_configuration(G, case):
     _run_and_check_all_paths(G, case)
 
 
+def _random_large_cases(n, seed):
+    """Seeded draws of calls of 1 to 2 times 1024 * 7168 row elements (T * H),
+    where the row kernels read rewritten rows through the cache whenever the
+    call has a delta and writes one of its source slots."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        H = int(rng.choice([7168, 7168, 8 * int(rng.integers(256, 2049))]))
+        t_min = -(-1024 * 7168 // H)
+        T = int(rng.integers(t_min, 2 * t_min + 1))
+        nb = int(rng.integers(1, 9))
+        cap = int(rng.integers(nb, 9))
+        widx = int(rng.choice([-1, int(rng.integers(0, nb)), int(rng.integers(0, nb)), int(rng.integers(0, cap))]))
+        slot_major = bool(rng.random() < 0.2)
+        cases.append(W.Case(
+            f"randlarge{seed}_{k}_H{H}_T{T}_nb{nb}_w{widx}", T=T, nb=nb, cap=cap, H=H,
+            has_delta=bool(rng.random() < 0.8), has_onorm=bool(rng.random() < 0.6), widx=widx,
+            token_pad=0 if slot_major else 8 * int(rng.integers(0, 5)),
+            row_pad=8 * int(rng.choice([0, 0, int(rng.integers(1, 40))])),
+            slot_major=slot_major, recipe=str(rng.choice(["normal", "soft"])),
+            seed=20_000 + 100 * seed + k))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_large_cases(10, 5), ids=lambda c: c.name)
+def test_random_large_configuration(G, case):
+    _run_and_check_all_paths(G, case)
+
+
 def test_soft_logits_mix(G):
     """O(1) logits so the mixture really mixes (the named workloads are nearly
     one-hot)."""
