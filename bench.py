@@ -164,8 +164,9 @@ def bench_mid(steps: int, warmup: int, eager: bool):
         ms = time_eager(calls, steps)
         reps = [ms]
     else:
+        # Six replays, each timing exactly `steps` calls; the median is reported.
         reps = time_graph(calls, steps, replays=6)
-        ms = reps[0]
+        ms = pct(reps, 50)
     per_call_ms = ms / steps
     per_call = [r / steps * 1e3 for r in reps]
     gbps = per_call_bytes / (per_call_ms * 1e-3) / 1e9
