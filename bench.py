@@ -166,8 +166,10 @@ def bench_mid(steps: int, warmup: int, eager: bool):
         ms = time_eager(calls, steps)
         reps = [ms]
     else:
-        # Six replays, each timing exactly `steps` calls; the median is reported.
-        reps = time_graph(calls, steps, replays=6)
+        # Six replays, each timing exactly `steps` calls, after three untimed
+        # ones (the first ~20 ms after building the inputs run a few percent
+        # slow); the median is reported.
+        reps = time_graph(calls, steps, replays=6, warm=3)
         ms = pct(reps, 50)
     per_call_ms = ms / steps
     per_call = [r / steps * 1e3 for r in reps]
