@@ -17,8 +17,9 @@
 //  * Row path (H = 7168, many tokens): one 448-lane workgroup (7 waves, two
 //    segments per lane) per token.  Per-lane fp32 sum-of-squares and query
 //    dot of every source (packed bf16 dot products), a 16-lane DPP reduction,
-//    a cross-row reduction through LDS, logits, the softmax (maximum, then
-//    the sum of exponentials, over at most 9 lanes), the fp32 mixture, the
+//    a cross-row reduction through LDS, logits, an online softmax (running
+//    maximum and rescaled sum, merged as a tree over at most 9 lanes), the
+//    fp32 mixture, the
 //    optional output RMSNorm (a second LDS reduction), bf16
 //    round-to-nearest-even stores.  With no bank rows the only source has
 //    weight 1: no logit, and at most the output norm's reduction.
@@ -475,23 +476,18 @@ __device__ __forceinline__ float sum_sq(const float (&y)[SPL][8]) {
   return s;
 }
 
-// Combines a[0..N) pairwise into a[0] (a[j] with a[j + w] for w = 1, 2, 4,
-// ...): a fixed order with a dependency depth of ceil(log2 N).
-template <int N, typename Op>
-__device__ __forceinline__ float tree_reduce(float (&a)[N], Op op) {
-#pragma unroll
-  for (int w = 1; w < N; w *= 2)
-#pragma unroll
-    for (int j = 0; j + w < N; j += 2 * w) a[j] = op(a[j], a[j + w]);
-  return a[0];
-}
-
-// Softmax over the NS sources.  Lane j (< NS) holds logit j; lane j of the
-// result holds p_j.  Two passes: the maximum m of the logits (exact in any
-// order), then each lane's exp(l_j - m) and their sum z; both read the NS
-// lanes' values and combine them in a fixed pairwise order, so every wave
-// obtains the same values.  All logits exist at this point, so the running
-// rescale of an online softmax would only lengthen the dependency chain.
+// Softmax over the NS sources, lane j (< NS) holding logit j; lane j of the
+// result holds p_j (lanes >= NS hold 0).  The normaliser is computed online:
+// each source enters as the pair (m, s) = (l_j, 1), a running maximum and the
+// sum of exp(l - m) over the sources it covers, and two pairs merge into
+// (max(m1, m2), s1 exp(m1 - max) + s2 exp(m2 - max)); one of the two factors
+// is exp(0) = 1, so a merge takes one exponential, exp(-|m1 - m2|), applied
+// to the side with the smaller maximum.  Every logit already sits in a lane,
+// so the merges run as a tree in a fixed pairwise order (depth
+// ceil(log2 NS)) rather than as a chain, and every wave obtains the same
+// (m, s).  Then p_j = exp(l_j - m) / s, with s >= 1 (the maximum's own term
+// is 1), so the hardware reciprocal serves.  A NaN logit makes s, hence
+// every p_j, NaN.
 template <int NS>
 __device__ __forceinline__ float softmax_lanes(float logit_lane) {
   if constexpr (NS == 1) {
@@ -500,15 +496,22 @@ __device__ __forceinline__ float softmax_lanes(float logit_lane) {
     return (logit_lane - logit_lane) + 1.f;
   } else {
     const int lane = threadIdx.x & (kWave - 1);
-    float a[NS];
+    float m[NS], s[NS];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) a[j] = lane_value(logit_lane, j);
-    const float m = tree_reduce(a, [](float x, float y) { return fmaxf(x, y); });
-    const float e = lane < NS ? __expf(logit_lane - m) : 0.f;
+    for (int j = 0; j < NS; ++j) {
+      m[j] = lane_value(logit_lane, j);
+      s[j] = 1.f;
+    }
 #pragma unroll
-    for (int j = 0; j < NS; ++j) a[j] = lane_value(e, j);
-    const float z = tree_reduce(a, [](float x, float y) { return x + y; });  // >= 1
-    return e * __builtin_amdgcn_rcpf(z);
+    for (int w = 1; w < NS; w *= 2)
+#pragma unroll
+      for (int j = 0; j + w < NS; j += 2 * w) {
+        const float d = m[j + w] - m[j];
+        const float e = __expf(-fabsf(d));
+        s[j] = d <= 0.f ? fmaf(s[j + w], e, s[j]) : fmaf(s[j], e, s[j + w]);
+        m[j] = fmaxf(m[j], m[j + w]);
+      }
+    return lane < NS ? __expf(logit_lane - m[0]) * __builtin_amdgcn_rcpf(s[0]) : 0.f;
   }
 }
 
