@@ -335,6 +335,44 @@ def bench_variant_sweep(T: int = 1024, windows: int = 4, steps: int = 120):
     return res
 
 
+def bench_configs(steps_min: int = 200):
+    """The reference case (T=4, nb=4, delta and output norm) and the 80-case
+    variant matrix (T in 1/16/256/2048 x nb in 0/4/8 x delta x output norm x
+    write slot in -1/nb-1), each as µs per call and algorithmic GB/s: one
+    resident input per T, its tokens split into windows of T that the graph
+    replay rotates over, enough of them to exceed the Infinity Cache."""
+    H = W.HIDDEN
+    res = {}
+    for T in (1, 4, 16, 256, 2048):
+        per_window = 2 * T * H * 11  # 8 bank slots, prefix, delta, out
+        windows = max(4, -(-2 * MALL_BYTES // per_window))
+        big = W.Case(f"configs_T{T}", T=T * windows, nb=8, widx=-1, seed=12)
+        s_all = Set(W.make_inputs(big))
+        cases = [W.pr1_ref()] if T == 4 else [c for c in W.variant_matrix() if c.T == T]
+        for c in cases:
+            def call(w, c=c):
+                sl = slice(w * T, (w + 1) * T)
+                A.attnres_fwd(s_all.prefix[sl], s_all.delta[sl] if c.has_delta else None,
+                              s_all.bank3[sl], c.nb, s_all.res_w, s_all.rms_w, c.eps,
+                              s_all.onw if c.has_onorm else None, c.oeps, c.widx, s_all.out[sl])
+
+            calls = [lambda w=w: call(w) for w in range(windows)]
+            for fn in calls[:8]:
+                fn()
+            torch.cuda.synchronize()
+            steps = max(steps_min, windows)
+            t = time_graph(calls, steps, replays=3, warm=2)
+            us = pct([x / steps * 1e3 for x in t], 50)
+            gbps = c.algorithmic_bytes() / us / 1e3
+            res[c.name] = dict(T=T, nb=c.nb, delta=c.has_delta, onorm=c.has_onorm, widx=c.widx,
+                               us=round(us, 3), GBps=round(gbps, 1),
+                               frac=round(gbps / HBM_PEAK_GBPS, 4))
+            log(f"config {c.name}: {us:.3f} us, {gbps:.0f} GB/s")
+        del s_all
+        torch.cuda.empty_cache()
+    return res
+
+
 CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
 CEILING_LIB = os.path.join(ROOT, "bench_ceiling.so")
 # The mid-prefill call's own buffers and row roles (ceiling_mid): 8 bank rows,
@@ -640,6 +678,8 @@ def main():
                     help="small batches: row vs split kernel over T and num_blocks")
     ap.add_argument("--variant-sweep", action="store_true",
                     help="only T=1024 calls over num_blocks x delta x output norm")
+    ap.add_argument("--configs", action="store_true",
+                    help="only the reference case (T=4, nb=4) and the 80-case variant matrix")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output directories")
     ap.add_argument("--profile-commands", default=None, help="JSON of the commands that made them")
@@ -670,6 +710,18 @@ def main():
     A.attnres_init()
     if args.calibrate:
         calibration_copy()
+    if args.configs:
+        table = bench_configs()
+        print(json.dumps({"metric": "attention-residual forward latency and throughput per case",
+                          "unit": "us/call", "higher_is_better": False, "data": "synthetic",
+                          "config": {"workload": "the reference case (T=4, nb=4, delta, output "
+                                                 "norm) and the variant matrix (T 1/16/256/2048 x "
+                                                 "nb 0/4/8 x delta x output norm x write slot "
+                                                 "-1/nb-1), H=7168, bf16",
+                                     "timing": "hipGraph replay, rotating token windows"},
+                          "cases": table, "kernel_source_hash": kernel_source_hash()}),
+              flush=True)
+        return
     if args.variant_sweep:
         sweep = bench_variant_sweep()
         print(json.dumps({"metric": "attention-residual forward throughput per variant",

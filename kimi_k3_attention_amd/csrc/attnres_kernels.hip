@@ -251,8 +251,8 @@ struct Token {
     if (!MASKED) return load_stream(q);
     return ok ? load_stream(q) : zero;
   }
-  // With CACHE_RW, the two rows a call also writes (prefix with a delta, and
-  // the bank slot widx when it is a source) are read through the cache at
+  // With CACHE_RW, the rows a call also writes (the bank slot widx, a source
+  // here, and prefix when a delta is given) are read through the cache at
   // normal priority, so that their writes find the lines resident, while rows
   // only read stream past the cache (load_row).  The slot is chosen at run
   // time, so its load sits in a uniform branch beside the streaming one; it
@@ -289,9 +289,10 @@ struct Token {
     const uint16_t *bank = p.blocks + t * p.tok_stride;
     const uint16_t *prow = p.prefix + t * p.prefix_stride;
     if constexpr (CACHE_RW) {
-      // Both in-place rows (prefix, and the written slot, a source here) are
-      // read through the cache; the slot is chosen at run time.
-      static_assert(DELTA && NB > 0, "two rewritten rows need a delta and a source slot");
+      // The in-place rows (the written slot, a source here, and prefix when
+      // a delta rewrites it) are read through the cache; the slot is chosen
+      // at run time.
+      static_assert(NB > 0, "a rewritten source row needs a source slot");
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const uint16_t *row = bank + j * p.slot_stride;
@@ -303,8 +304,13 @@ struct Token {
           for (int i = 0; i < SPL; ++i) x[j][i] = load_row(at(row, sb[i]), ok[i]);
         }
       }
+      if constexpr (DELTA) {
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) x[NB][i] = load_rewritten(p, prow, sb[i]);
+        for (int i = 0; i < SPL; ++i) x[NB][i] = load_rewritten(p, prow, sb[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(at(prow, sb[i]), ok[i]);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < NB; ++j)
@@ -1036,8 +1042,10 @@ using KernelFn = void (*)(KParams);
 template <int NB>
 KernelFn row_fn(bool d, bool o, bool cache_rw) {
   if constexpr (NB > 0)
-    if (d && cache_rw)
-      return o ? attnres_row_kernel<NB, true, true, true> : attnres_row_kernel<NB, true, false, true>;
+    if (cache_rw) {
+      if (d) return o ? attnres_row_kernel<NB, true, true, true> : attnres_row_kernel<NB, true, false, true>;
+      return o ? attnres_row_kernel<NB, false, true, true> : attnres_row_kernel<NB, false, false, true>;
+    }
   if (d) return o ? attnres_row_kernel<NB, true, true> : attnres_row_kernel<NB, true, false>;
   return o ? attnres_row_kernel<NB, false, true> : attnres_row_kernel<NB, false, false>;
 }
@@ -1050,9 +1058,13 @@ KernelFn split_fn(bool d, bool o) {
 template <int SPL, bool MASKED, int NB>
 KernelFn anyh_fn(bool d, bool o, bool cache_rw) {
   if constexpr (NB > 0)
-    if (d && cache_rw)
-      return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, true>
-               : attnres_anyh_kernel<SPL, MASKED, NB, true, false, true>;
+    if (cache_rw) {
+      if (d)
+        return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, true>
+                 : attnres_anyh_kernel<SPL, MASKED, NB, true, false, true>;
+      return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, true>
+               : attnres_anyh_kernel<SPL, MASKED, NB, false, false, true>;
+    }
   if (d)
     return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true>
              : attnres_anyh_kernel<SPL, MASKED, NB, true, false>;
@@ -1086,12 +1098,15 @@ enum class Kind { kRow, kSplit, kAnyH };
 // kernel between about 4 and 8 million elements from H = 2048 to 16384.
 constexpr int64_t kCacheRewrittenMinElems = int64_t(1024) * 7168;
 
-// Whether a row-kernel call reads its two rewritten rows through the cache:
-// it has a delta (prefix is rewritten), writes a slot that is also a source,
-// and is large enough.
+// Whether a row-kernel call reads its rewritten rows through the cache: it
+// writes a bank slot that is also a source, and is large enough.  With a
+// delta, prefix is rewritten too; with the written slot as the only such
+// row the gain starts at about twice the size (T = 1024 at H = 7168 was
+// +2 % at nb = 4 and -2 % at nb = 8; T = 2048 +3-6 %, T = 4096 +5-12 %).
 bool cache_rewritten(const FwdArgs &a) {
-  return a.delta != nullptr && a.block_write_idx >= 0 && a.block_write_idx < a.num_blocks &&
-         a.T * a.H >= kCacheRewrittenMinElems;
+  if (a.block_write_idx < 0 || a.block_write_idx >= a.num_blocks) return false;
+  const int64_t min_elems = a.delta != nullptr ? kCacheRewrittenMinElems : 2 * kCacheRewrittenMinElems;
+  return a.T * a.H >= min_elems;
 }
 
 // attnres_fwd's choice of kernel at H = 7168, from measured latency per call
@@ -1289,11 +1304,10 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
     return e == hipSuccess ? ATTNRES_OK : hip_fail(e);
   }
 
-  // Reading the two rows a call also writes (prefix with a delta, and a
-  // written slot that is a source) through the cache pays once a call
-  // streams many tokens: T = 1024, nb = 8: 33.7 -> 32.6 us, T = 4096:
-  // 131 -> 117 us.  Below about 1024 tokens (latency-bound), or with one
-  // such row, streaming reads are faster.
+  // Reading the rows a call also writes (a written slot that is a source,
+  // and prefix with a delta) through the cache pays once a call streams many
+  // tokens: T = 1024, nb = 8, with a delta: 33.7 -> 32.6 us, T = 4096:
+  // 131 -> 117 us.  Smaller calls (latency-bound) read them streaming.
   const bool cache_rw = kind == Kind::kRow && cache_rewritten(a);
   KernelFn fn = pick(kind, a.num_blocks, has_d, has_o, cache_rw);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;

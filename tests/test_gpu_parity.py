@@ -411,6 +411,12 @@ CACHED_REWRITE_CASES = [
     dict(H=2880, T=2560, nb=4, widx=2),                       # masked rows
     dict(H=16376, T=449, nb=2, widx=1, has_onorm=False),      # four segments per lane, masked
     dict(H=12288, T=600, nb=6, widx=5, token_pad=64),
+    # no delta: only the written slot is read through the cache (T * H at or
+    # above 2 * 1024 * 7168)
+    dict(T=2048, nb=4, widx=3, has_delta=False),
+    dict(T=2100, nb=8, widx=7, has_delta=False, has_onorm=False, token_pad=64),
+    dict(H=8192, T=1800, nb=6, widx=2, has_delta=False),
+    dict(H=2880, T=5200, nb=3, widx=0, has_delta=False),             # masked rows
 ]
 
 
