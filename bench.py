@@ -693,7 +693,7 @@ def main():
         summarize_profile(*args.summarize_profile, commands=json.loads(args.profile_commands or "{}"))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the attention-residual op shards by tokens with no exchange, so the "
               "single-GPU figure is the per-GPU rate", file=sys.stderr)
         sys.exit(2)
