@@ -7,7 +7,9 @@
 // per token it reads num_blocks + 1 (+1 with a delta) rows of H bf16 once,
 // reduces each row to two scalars, and writes 1-3 rows.  Arithmetic intensity
 // is about 2 flop/byte, far below the fp32 ridge, so HBM bandwidth bounds it
-// and no matrix core is involved.
+// and the streaming reduction uses no matrix core.  The one dense contraction
+// is the split path's Gram matrix of a part's rows (for the output norm),
+// formed on the matrix cores when it is large.
 //
 // Layout of the work: a "segment" is 8 consecutive bf16 (16 bytes); a row of
 // 7168 is 896 segments.  A lane owns one or more segments of every source row
@@ -69,6 +71,9 @@
 #ifndef ATTNRES_SPLIT_DPP_WORDS
 #define ATTNRES_SPLIT_DPP_WORDS 8       // split path: words summed by DPP instead of via LDS
 #endif
+#ifndef ATTNRES_SPLIT_MFMA_WORDS
+#define ATTNRES_SPLIT_MFMA_WORDS 40     // split path: from this many words, one matrix-core product
+#endif
 #ifndef ATTNRES_EARLY_CUR_STORE
 #define ATTNRES_EARLY_CUR_STORE 0       // write prefix / bank rows as soon as cur exists
 #endif
@@ -79,6 +84,8 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSeg = 8;                       // bf16 per 16-byte segment
 constexpr int kSegs = kHidden / kSeg;         // 896 segments per row
@@ -947,7 +954,10 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   // Per-lane values summed over the wave, then published with one store of
   // tagged words (lane v holds word v).  A few words are summed with DPP
   // wave reductions (independent chains); more are transposed through LDS so
-  // that lane v sums value v over the wave.
+  // that lane v sums value v over the wave; the most (an output norm's Gram
+  // matrix at nb >= 7) come from one matrix-core product.  Measured at T = 1
+  // with an output norm, transposition / product: nb = 5 4.47 / 4.54 us,
+  // nb = 6 4.71 / 4.72, nb = 7 4.84 / 4.79, nb = 8 5.07 / 4.89.
   if constexpr (NV <= ATTNRES_SPLIT_DPP_WORDS) {
     float ss[NS], dq[NS], val[NV];
     tk.partials(qh, ql, ss, dq);
@@ -977,6 +987,67 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     }
     tk.keep_packed();
     if (lane < NV) tagged_store(slot + lane, word, gen);
+  } else if constexpr (NV >= ATTNRES_SPLIT_MFMA_WORDS) {
+    // X: the part's rows over its 512 elements -- the NS sources, then q_hi
+    // and q_lo -- so that G = X X^T holds every sum this part publishes: the
+    // Gram matrix of the sources (sums of squares on its diagonal) and, in
+    // rows NS and NS + 1, the two halves of the query dots.  Each lane parks
+    // its 16-byte segment of every row in LDS.  16 matrix-core steps of 32
+    // elements (v_mfma_f32_16x16x32_bf16, one register as both A and B) then
+    // read X in the operand layout, lane l supplying row l % 16 and elements
+    // 32 c + 8 (l / 16) .. + 8 of step c (rows from NR on are zero), and lane
+    // l ends with G[4 (l / 16) + i][l % 16] in accumulator element i.  The
+    // products of bf16 values are exact in fp32, as in the dot products.
+    constexpr int NR = NS + 2;
+    static_assert(NR <= 16, "the rows of one 16 x 16 product");
+    constexpr int kSteps = kPartThreads * kSeg / 32;
+    constexpr int kXStride = kPartThreads * kSeg + kSeg;  // +16 B: conflict-free 128-bit accesses
+    __shared__ __align__(16) uint16_t s_x[NR][kXStride];
+    __shared__ __align__(16) float s_g[16][17];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) *reinterpret_cast<u32x4 *>(&s_x[j][lane * kSeg]) = tk.x[j][0];
+    *reinterpret_cast<u32x4 *>(&s_x[NS][lane * kSeg]) = qh[0];
+    *reinterpret_cast<u32x4 *>(&s_x[NS + 1][lane * kSeg]) = ql[0];
+    tk.keep_packed();
+    __syncthreads();
+    const int r = lane & 15, kb = lane >> 4;
+    const int rr = r < NR ? r : 0;  // rows from NR on read row 0, then count as zero
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kSteps; c += 2) {
+      u32x4 w0 = *reinterpret_cast<const u32x4 *>(&s_x[rr][32 * c + 8 * kb]);
+      u32x4 w1 = *reinterpret_cast<const u32x4 *>(&s_x[rr][32 * (c + 1) + 8 * kb]);
+      w0 = r < NR ? w0 : zero;
+      w1 = r < NR ? w1 : zero;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, w0), a1 = __builtin_bit_cast(bf16x8, w1);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, a0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, a1, acc1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_g[4 * kb + i][r] = acc0[i] + acc1[i];
+    __syncthreads();
+    // Lane v takes word v: a Gram entry (pairs j <= k in row-major order) or
+    // a sum of squares, then the query dots.
+    float word = 0.f;
+    if (lane < NV) {
+      if (lane >= Words::kDot) {
+        const int j = lane - Words::kDot;
+        word = s_g[NS][j] + s_g[NS + 1][j];
+      } else if (ONORM) {
+        int j = 0, rem = lane;
+#pragma unroll
+        for (int q = 0; q < NS; ++q)
+          if (rem >= NS - j && j < NS - 1) {
+            rem -= NS - j;
+            ++j;
+          }
+        word = s_g[j][j + rem];
+      } else {
+        word = s_g[lane][lane];
+      }
+      tagged_store(slot + lane, word, gen);
+    }
   } else {
   {
     float ss[NS], dq[NS];

@@ -428,6 +428,17 @@ def test_cached_rewritten_rows(G, kw):
     _run_and_check_all_paths(G, case)
 
 
+@pytest.mark.parametrize("nb", range(1, 9))
+@pytest.mark.parametrize("onorm", [False, True])
+def test_split_word_paths(G, nb, onorm):
+    """Every way the split path sums its per-part words: DPP wave sums (few
+    words), the LDS transposition, and the matrix-core Gram product (an
+    output norm at nb >= 7), on a few tokens, against the oracle."""
+    case = W.Case(f"split_words_nb{nb}_o{int(onorm)}", T=3, nb=nb, has_onorm=onorm,
+                  widx=nb - 1, recipe="soft", seed=70 + nb + 10 * onorm)
+    _run_and_check_all_paths(G, case)
+
+
 def test_slot_major_bank(G):
     case = W.Case("slot_major_T40_nb6", T=40, nb=6, widx=6, slot_major=True, seed=51)
     _run_and_check_all_paths(G, case)
