@@ -28,8 +28,9 @@
 //  * Split path (H = 7168, few tokens): 14 single-wave workgroups per token,
 //    each owning 512 elements of every row, so one token is spread over 14
 //    CUs.  Per-part sums (and, with an output norm, the sources' Gram matrix),
-//    summed over the wave by DPP (few words) or an LDS transposition (many),
-//    are exchanged once through a device workspace of self-validating tagged
+//    summed over the wave by DPP (few words), an LDS transposition (more) or
+//    one matrix-core product X X^T of the part's rows (the most, nb >= 7 with
+//    a norm), are exchanged once through a device workspace of self-validating tagged
 //    words read and written with agent-scope atomics (the 8 XCDs do not share
 //    L2); no reset is needed between calls or graph replays.  Waits are
 //    bounded: a wait that gives up raises a device flag instead of hanging.
@@ -37,7 +38,8 @@
 //    path's steps with a runtime row length, 64-512 lanes per token and two
 //    or four segments per lane; segments past the row end are masked.
 //
-// Compile-time specialisation on num_blocks (0..8), delta and output norm;
+// Compile-time specialisation on num_blocks (0..8), delta and output norm,
+// and on whether the rows a call rewrites are read through the cache;
 // block_write_idx stays a uniform runtime branch.  Row strides of prefix,
 // delta and out are runtime values.
 #include <hip/hip_runtime.h>
