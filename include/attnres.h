@@ -68,7 +68,7 @@ extern "C" {
 
 /* ---- path selectors for attnres_fwd_path -------------------------------- */
 #define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: at H = 7168 split for T up to
-                                -/40/48/64/64/80/80/64/64 with 0..8 blocks (never with
+                                -/40/40/56/64/64/64/80/80 with 0..8 blocks (never with
                                 0 blocks), else row; other H: any-H */
 #define ATTNRES_PATH_ROW 1   /* one workgroup per token (the any-H kernel when H != 7168) */
 #define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (H = 7168, T <= 256) */

@@ -1187,7 +1187,7 @@ bool cache_rewritten(const FwdArgs &a) {
 // 14 CUs (split) beats one CU per token (row) up to this many tokens, by
 // block count.  A single source (nb = 0) needs no exchange on the row path,
 // which is then faster at every T.
-constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 48, 64, 64, 80, 80, 64, 64};
+constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 40, 56, 64, 64, 64, 80, 80};
 static_assert(80 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
 Kind auto_kind(int64_t T, int nb) { return T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow; }
 
