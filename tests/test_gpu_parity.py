@@ -328,7 +328,8 @@ def _random_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", _random_cases(40, 1) + _random_cases(80, 2), ids=lambda c: c.name)
+@pytest.mark.parametrize("case", _random_cases(40, 1) + _random_cases(80, 2) + _random_cases(150, 4),
+                         ids=lambda c: c.name)
 def test_random_configuration(G, case):
     _run_and_check_all_paths(G, case)
 
@@ -357,7 +358,8 @@ def _random_large_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", _random_large_cases(10, 5), ids=lambda c: c.name)
+@pytest.mark.parametrize("case", _random_large_cases(10, 5) + _random_large_cases(10, 6),
+                         ids=lambda c: c.name)
 def test_random_large_configuration(G, case):
     _run_and_check_all_paths(G, case)
 
