@@ -30,7 +30,8 @@
  * neither read nor written.
  *
  * Hidden size: any H that is a multiple of 8, up to ATTNRES_MAX_HIDDEN.  H =
- * 7168 (Kimi-K3) runs on tuned kernels; other sizes on one any-H row kernel.
+ * 7168 (Kimi-K3) runs on tuned kernels; other sizes on one any-H row kernel,
+ * and above 7168 small batches also on the split kernel.
  *
  * Tensors are bf16 (passed as raw 16-bit patterns) in device memory.  The
  * library keeps no pointer after a call returns; the caller owns every buffer
@@ -69,9 +70,11 @@ extern "C" {
 /* ---- path selectors for attnres_fwd_path -------------------------------- */
 #define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: at H = 7168 split for T up to
                                 -/40/40/56/64/64/64/80/80 with 0..8 blocks (never with
-                                0 blocks), else row; other H: any-H */
+                                0 blocks), else row; above 7168 split for T <= 48 with
+                                1..8 blocks, else any-H; below 7168 any-H */
 #define ATTNRES_PATH_ROW 1   /* one workgroup per token (the any-H kernel when H != 7168) */
-#define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (H = 7168, T <= 256) */
+#define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (H >= 7168,
+                                T <= 256) */
 #define ATTNRES_PATH_ANY_H 3 /* the any-H row kernel, also at H = 7168 */
 
 /* Largest T the split path accepts (its per-device workspace). */

@@ -785,6 +785,8 @@ AnyShape anyh_shape(int64_t H) {
   return {spl, waves * kWave, nseg % reach != 0};
 }
 static_assert(4 * kAnyMaxThreads * kSeg >= kMaxHidden, "any-H kernel must reach the largest H");
+static_assert(3 * kParts * kPartThreads * kSeg >= kMaxHidden,
+              "three segments per lane of the split path must reach the largest H");
 
 // ---------------------------------------------------------------------------
 // split path: kParts single-wave workgroups per token
@@ -868,13 +870,14 @@ constexpr float kGramGuard = 1.f / 16.f;
 // The mixture weights from a token's exchanged totals (lane v < NV holds word
 // v): lane j < NS returns p_j; ss_j receives lane j's sum of squares.
 template <int NS, bool ONORM>
-__device__ __forceinline__ float weights_from_totals(float total, float rms_eps, float &ss_j) {
+__device__ __forceinline__ float weights_from_totals(float total, float rms_eps, float inv_h,
+                                                    float &ss_j) {
   using Words = SplitWords<NS, ONORM>;
   const int lane = threadIdx.x & (kWave - 1);
   const int jl = lane < NS ? lane : 0;
   ss_j = lane_shuffle(total, Words::ss_word(jl));
   const float dq_j = lane_shuffle(total, Words::kDot + jl);
-  const float logit = lane < NS ? dq_j * rsqrtf(ss_j * kInvHidden + rms_eps) : 0.f;
+  const float logit = lane < NS ? dq_j * rsqrtf(ss_j * inv_h + rms_eps) : 0.f;
   return softmax_lanes<NS>(logit);
 }
 
@@ -903,7 +906,7 @@ __device__ __forceinline__ void gram_ysq(float total, float p_lane, float ss_j, 
   b = lane_value(wave_sum_lane63(bound), kWave - 1);
 }
 
-template <int NB, bool DELTA, bool ONORM>
+template <int NB, bool DELTA, bool ONORM, int SPL = 1, bool MASKED = false>
 __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) {
   constexpr int NS = NB + 1;
   using Words = SplitWords<NS, ONORM>;
@@ -915,6 +918,11 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   const int64_t t = blockIdx.x / kParts;
   const int part = blockIdx.x - int(t) * kParts;
   const int lane = threadIdx.x;
+  // Part `part` owns SPL segments per lane, part * 64 * SPL + lane + 64 i; at
+  // H = 7168, one (512 elements per part).
+  const int seg0 = part * kPartThreads * SPL + lane;
+  constexpr int seg_step = kPartThreads;
+  const float inv_h = SPL == 1 && !MASKED ? kInvHidden : p.inv_h;
   uint64_t *const tok_ws = p.ws_part + size_t(t) * kParts * kSlot;
   uint64_t *const slot = tok_ws + part * kSlot;
 
@@ -925,33 +933,33 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     // norm nothing is exchanged.
     uint32_t gen0 = 0;
     if constexpr (ONORM) gen0 = tag_of(tagged_load(slot)) + 1u;
-    Token<NB, DELTA, ONORM, 1> tk;
-    tk.issue(p, t, part * kPartThreads + lane, 0);
+    Token<NB, DELTA, ONORM, SPL, MASKED> tk;
+    tk.issue(p, t, seg0, seg_step);
     tk.finish_cur();
-    tk.issue_onw(p, part * kPartThreads + lane, 0);
-    float y[1][8];
+    tk.issue_onw(p, seg0, seg_step);
+    float y[SPL][8];
     tk.cur_as_mix(y);
     float rsig = 1.f;
     if constexpr (ONORM) {
-      const float s = wave_sum_lane63(sum_sq<1>(y));
+      const float s = wave_sum_lane63(sum_sq<SPL>(y));
       if (lane == kWave - 1) tagged_store(slot, s, gen0);
       float total = 0.f;
       if (lane == 0) total = gather(tok_ws, 0, gen0, p.ws_flag);
-      rsig = rsqrtf(lane_value(total, 0) * kInvHidden + p.out_eps);
+      rsig = rsqrtf(lane_value(total, 0) * inv_h + p.out_eps);
     }
-    tk.store(p, t, part * kPartThreads + lane, 0, y, rsig);
+    tk.store(p, t, seg0, seg_step, y, rsig);
     return;
   }
 
   // This call's generation (issued first; used only when publishing).
   const uint32_t gen = tag_of(tagged_load(slot)) + 1u;
 
-  Token<NB, DELTA, ONORM, 1> tk;
-  tk.issue(p, t, part * kPartThreads + lane, 0);
-  u32x4 qh[1], ql[1];
+  Token<NB, DELTA, ONORM, SPL, MASKED> tk;
+  tk.issue(p, t, seg0, seg_step);
+  u32x4 qh[SPL], ql[SPL];
   tk.query(qh, ql);
   tk.finish_cur();
-  if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, part * kPartThreads + lane, 0);
+  if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, seg0, seg_step);
 
   // Per-lane values summed over the wave, then published with one store of
   // tagged words (lane v holds word v).  A few words are summed with DPP
@@ -971,7 +979,9 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
         for (int k = j + 1; k < NS; ++k) {
           float g = 0.f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) g = dot2(tk.x[j][0][w], tk.x[k][0][w], g);
+          for (int i = 0; i < SPL; ++i)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) g = dot2(tk.x[j][i][w], tk.x[k][i][w], g);
           val[pair_row_start(NS, j) + (k - j)] = g;
         }
       }
@@ -1002,14 +1012,19 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     // products of bf16 values are exact in fp32, as in the dot products.
     constexpr int NR = NS + 2;
     static_assert(NR <= 16, "the rows of one 16 x 16 product");
-    constexpr int kSteps = kPartThreads * kSeg / 32;
-    constexpr int kXStride = kPartThreads * kSeg + kSeg;  // +16 B: conflict-free 128-bit accesses
+    constexpr int kSteps = kPartThreads * SPL * kSeg / 32;
+    constexpr int kXStride = kPartThreads * SPL * kSeg + kSeg;  // +16 B: conflict-free 128-bit accesses
     __shared__ __align__(16) uint16_t s_x[NR][kXStride];
     __shared__ __align__(16) float s_g[16][17];
+    // (segments past a masked row's end hold zeros and add nothing)
 #pragma unroll
-    for (int j = 0; j < NS; ++j) *reinterpret_cast<u32x4 *>(&s_x[j][lane * kSeg]) = tk.x[j][0];
-    *reinterpret_cast<u32x4 *>(&s_x[NS][lane * kSeg]) = qh[0];
-    *reinterpret_cast<u32x4 *>(&s_x[NS + 1][lane * kSeg]) = ql[0];
+    for (int i = 0; i < SPL; ++i) {
+      const int e = (i * kPartThreads + lane) * kSeg;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) *reinterpret_cast<u32x4 *>(&s_x[j][e]) = tk.x[j][i];
+      *reinterpret_cast<u32x4 *>(&s_x[NS][e]) = qh[i];
+      *reinterpret_cast<u32x4 *>(&s_x[NS + 1][e]) = ql[i];
+    }
     tk.keep_packed();
     __syncthreads();
     const int r = lane & 15, kb = lane >> 4;
@@ -1062,7 +1077,9 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
         for (int k = j + 1; k < NS; ++k) {
           float g = 0.f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) g = dot2(tk.x[j][0][w], tk.x[k][0][w], g);
+          for (int i = 0; i < SPL; ++i)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) g = dot2(tk.x[j][i][w], tk.x[k][i][w], g);
           s_tr[pair_row_start(NS, j) + (k - j)][lane] = g;
         }
       }
@@ -1081,12 +1098,12 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   }
   }
 
-  tk.issue_onw(p, part * kPartThreads + lane, 0);
+  tk.issue_onw(p, seg0, seg_step);
   // The token's totals: lane v holds word v summed over the parts.
   const float total = lane < NV ? gather(tok_ws, lane, gen, p.ws_flag) : 0.f;
   float ss_j;
-  const float p_lane = weights_from_totals<NS, ONORM>(total, p.rms_eps, ss_j);
-  float y[1][8];
+  const float p_lane = weights_from_totals<NS, ONORM>(total, p.rms_eps, inv_h, ss_j);
+  float y[SPL][8];
   tk.keep_packed();
   tk.mix(p_lane, y);
 
@@ -1097,13 +1114,13 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     float tot = ysq;
     if (!(ysq >= kGramGuard * b * b)) {
       // Every part sees the same totals and takes the same branch.
-      const float sy = wave_sum_lane63(sum_sq<1>(y));
+      const float sy = wave_sum_lane63(sum_sq<SPL>(y));
       if (lane == kWave - 1) tagged_store(slot + kSlotYsq, sy, gen);
       tot = gather(tok_ws, kSlotYsq, gen, p.ws_flag);
     }
-    rsig = rsqrtf(tot * kInvHidden + p.out_eps);
+    rsig = rsqrtf(tot * inv_h + p.out_eps);
   }
-  tk.store(p, t, part * kPartThreads + lane, 0, y, rsig);
+  tk.store(p, t, seg0, seg_step, y, rsig);
 }
 
 // ---------------------------------------------------------------------------
@@ -1126,6 +1143,26 @@ template <int NB>
 KernelFn split_fn(bool d, bool o) {
   if (d) return o ? attnres_split_kernel<NB, true, true> : attnres_split_kernel<NB, true, false>;
   return o ? attnres_split_kernel<NB, false, true> : attnres_split_kernel<NB, false, false>;
+}
+// The split path above 7168: SPL segments per lane per part, masked at the
+// row end.
+template <int NB, int SPL>
+KernelFn split_wide_fn(bool d, bool o) {
+  if (d)
+    return o ? attnres_split_kernel<NB, true, true, SPL, true>
+             : attnres_split_kernel<NB, true, false, SPL, true>;
+  return o ? attnres_split_kernel<NB, false, true, SPL, true>
+           : attnres_split_kernel<NB, false, false, SPL, true>;
+}
+KernelFn pick_split_wide(int nb, bool d, bool o, int spl) {
+  switch (nb) {
+#define ATTNRES_CASE(N) \
+  case N: return spl == 2 ? split_wide_fn<N, 2>(d, o) : split_wide_fn<N, 3>(d, o);
+    ATTNRES_CASE(0) ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
+    ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
+#undef ATTNRES_CASE
+    default: return nullptr;
+  }
 }
 
 template <int SPL, bool MASKED, int NB>
@@ -1190,6 +1227,11 @@ bool cache_rewritten(const FwdArgs &a) {
 constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 40, 56, 64, 64, 64, 80, 80};
 static_assert(80 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
 Kind auto_kind(int64_t T, int nb) { return T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow; }
+// Above H = 7168 (2-3 segments per lane and part) the split path wins up to
+// about 48 tokens with 1-8 blocks; beyond, its parts hold too many registers
+// and the any-H row kernel is faster (H = 16384, nb = 8: T = 48 split 10.4
+// against 13.4 us, T = 80 17.9 against 14.0 us).
+constexpr int kSplitMaxTWide = 48;
 
 KernelFn pick(Kind kind, int nb, bool d, bool o, bool cache_rw) {
   switch (nb) {
@@ -1296,14 +1338,22 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   if (a.T == 0) return ATTNRES_OK;
 
   // The tuned kernels are built for H = 7168; every other H runs the any-H
-  // row kernel, which can also be forced at 7168.
+  // row kernel, which can also be forced at 7168.  Above 7168 the split path
+  // also runs, its 14 parts taking 2 or 3 segments per lane (masked at the
+  // row end), and the automatic choice uses it for the same small batches.
   const bool tuned = a.H == kHidden;
-  if (path == ATTNRES_PATH_SPLIT && !tuned) return ATTNRES_E_UNSUPPORTED;
+  const bool wide = a.H > kHidden;
+  const int split_spl = wide ? int((a.H / kSeg + kParts * kPartThreads - 1) / (kParts * kPartThreads)) : 1;
+  if (path == ATTNRES_PATH_SPLIT && !tuned && !wide) return ATTNRES_E_UNSUPPORTED;
   Kind kind;
-  if (path == ATTNRES_PATH_ANY_H || !tuned)
+  if (path == ATTNRES_PATH_ANY_H)
     kind = Kind::kAnyH;
   else if (path == ATTNRES_PATH_SPLIT)
     kind = Kind::kSplit;
+  else if (!tuned)
+    kind = path == ATTNRES_PATH_AUTO && wide && a.num_blocks > 0 && a.T <= kSplitMaxTWide
+               ? Kind::kSplit
+               : Kind::kAnyH;
   else if (path == ATTNRES_PATH_ROW)
     kind = Kind::kRow;
   else
@@ -1382,7 +1432,8 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   // tokens: T = 1024, nb = 8, with a delta: 33.7 -> 32.6 us, T = 4096:
   // 131 -> 117 us.  Smaller calls (latency-bound) read them streaming.
   const bool cache_rw = kind == Kind::kRow && cache_rewritten(a);
-  KernelFn fn = pick(kind, a.num_blocks, has_d, has_o, cache_rw);
+  KernelFn fn = split && wide ? pick_split_wide(a.num_blocks, has_d, has_o, split_spl)
+                              : pick(kind, a.num_blocks, has_d, has_o, cache_rw);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;
   unsigned row_grid = unsigned(a.T);
   const int wpc = row_wgs_per_cu(a.num_blocks);

@@ -28,10 +28,11 @@ def _paths(T, H=7168):
     """Every kernel that can run a call of T tokens at hidden size H: at 7168
     the tuned row kernel, the split kernel (T <= 256) and the any-H kernel;
     at other sizes the any-H kernel (through the automatic choice, the row
-    selector and its own)."""
+    selector and its own), and above 7168 also the split kernel with 2 or 3
+    segments per lane (T <= 256)."""
     from kimi_k3_attention_amd import attnres as A
     ps = [None, A.ATTNRES_PATH_ROW, A.ATTNRES_PATH_ANY_H]
-    if H == 7168 and T <= A.ATTNRES_SPLIT_MAX_TOKENS:
+    if H >= 7168 and T <= A.ATTNRES_SPLIT_MAX_TOKENS:
         ps.append(A.ATTNRES_PATH_SPLIT)
     return ps
 
@@ -223,7 +224,9 @@ def test_large_rows_back_to_back(G):
     assert A.attnres_device_status() == A.ATTNRES_OK
 
 
-def test_split_path_refuses_other_hidden_sizes(G):
+def test_split_path_refuses_smaller_hidden_sizes(G):
+    """The split path runs at 7168 and above; below, forcing it is an error
+    that touches nothing."""
     from kimi_k3_attention_amd import attnres as A
     case = W.other_hidden(4096, T=4, nb=2)
     inp = W.make_inputs(case)
@@ -427,6 +430,27 @@ CACHED_REWRITE_CASES = [
 def test_cached_rewritten_rows(G, kw):
     kw = dict(kw)
     case = W.Case(f"cached_rw_T{kw['T']}", seed=60 + kw["T"] % 97, **kw)
+    _run_and_check_all_paths(G, case)
+
+
+WIDE_SPLIT_CASES = [
+    dict(H=7176, T=3, nb=8),                          # one segment past 7168: two per lane, masked
+    dict(H=8192, T=1, nb=7),
+    dict(H=9000, T=5, nb=1, has_onorm=False),
+    dict(H=12288, T=40, nb=4, widx=-1),
+    dict(H=14336, T=2, nb=8),                         # two segments per lane, every lane full
+    dict(H=14344, T=3, nb=7),                         # three per lane
+    dict(H=16384, T=16, nb=8, has_delta=False),
+    dict(H=16376, T=1, nb=0),
+]
+
+
+@pytest.mark.parametrize("kw", WIDE_SPLIT_CASES, ids=lambda kw: f"H{kw['H']}_T{kw['T']}_nb{kw['nb']}")
+def test_wide_split(G, kw):
+    """The split path above 7168 (2 or 3 segments per lane per part, masked at
+    the row end), every word path, against the oracle with every kernel."""
+    kw = dict(kw)
+    case = W.other_hidden(kw.pop("H"), kw.pop("T"), kw.pop("nb"), **kw)
     _run_and_check_all_paths(G, case)
 
 
