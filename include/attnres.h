@@ -202,6 +202,13 @@ const char *attnres_strerror(int status);
 /* The hipError_t of the last failed HIP call in this library (0 if none). */
 int attnres_last_hip_error(void);
 
+/* The kernel attnres_fwd (ATTNRES_PATH_AUTO) runs for a call of T tokens,
+ * hidden size H and num_blocks block rows: ATTNRES_PATH_ROW (the tuned row
+ * kernel, H = 7168), ATTNRES_PATH_SPLIT or ATTNRES_PATH_ANY_H; or
+ * ATTNRES_E_SHAPE, ATTNRES_E_UNSUPPORTED or ATTNRES_E_NUM_BLOCKS for sizes
+ * attnres_fwd rejects.  Host only: makes no HIP call. */
+int attnres_auto_path(int64_t T, int64_t H, int num_blocks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,6 +72,8 @@ _lib.attnres_strerror.argtypes = [_int]
 _lib.attnres_strerror.restype = ctypes.c_char_p
 _lib.attnres_last_hip_error.argtypes = []
 _lib.attnres_last_hip_error.restype = _int
+_lib.attnres_auto_path.argtypes = [_i64, _i64, _int]
+_lib.attnres_auto_path.restype = _int
 
 
 def lib() -> ctypes.CDLL:
@@ -237,3 +239,12 @@ def attnres_strerror(status: int) -> str:
 
 def attnres_last_hip_error() -> int:
     return _lib.attnres_last_hip_error()
+
+
+def attnres_auto_path(T: int, H: int, num_blocks: int) -> int:
+    """The ATTNRES_PATH_* kernel that attnres_fwd runs for these sizes
+    (host only); raises AttnResError for sizes it rejects."""
+    rc = _lib.attnres_auto_path(int(T), int(H), int(num_blocks))
+    if rc < 0:
+        raise AttnResError(rc, "attnres_auto_path")
+    return rc

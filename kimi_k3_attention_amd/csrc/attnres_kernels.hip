@@ -1229,12 +1229,21 @@ bool cache_rewritten(const FwdArgs &a) {
 // which is then faster at every T.
 constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 40, 56, 64, 64, 64, 80, 80};
 static_assert(80 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
-Kind auto_kind(int64_t T, int nb) { return T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow; }
+Kind auto_kind(int64_t T, int nb) {
+  return nb > 0 && T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow;
+}
 // Above H = 7168 (2-3 segments per lane and part) the split path wins up to
 // about 48 tokens with 1-8 blocks; beyond, its parts hold too many registers
 // and the any-H row kernel is faster (H = 16384, nb = 8: T = 48 split 10.4
 // against 13.4 us, T = 80 17.9 against 14.0 us).
 constexpr int kSplitMaxTWide = 48;
+
+// The kernel attnres_fwd runs for T tokens, hidden size H and nb block rows.
+Kind auto_choice(int64_t T, int64_t H, int nb) {
+  if (H == kHidden) return auto_kind(T, nb);
+  if (H > kHidden && nb > 0 && T <= kSplitMaxTWide) return Kind::kSplit;
+  return Kind::kAnyH;
+}
 
 KernelFn pick(Kind kind, int nb, bool d, bool o, bool cache_rw) {
   switch (nb) {
@@ -1353,14 +1362,10 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
     kind = Kind::kAnyH;
   else if (path == ATTNRES_PATH_SPLIT)
     kind = Kind::kSplit;
-  else if (!tuned)
-    kind = path == ATTNRES_PATH_AUTO && wide && a.num_blocks > 0 && a.T <= kSplitMaxTWide
-               ? Kind::kSplit
-               : Kind::kAnyH;
   else if (path == ATTNRES_PATH_ROW)
-    kind = Kind::kRow;
+    kind = tuned ? Kind::kRow : Kind::kAnyH;
   else
-    kind = auto_kind(a.T, a.num_blocks);
+    kind = auto_choice(a.T, a.H, a.num_blocks);
   const bool any_h = kind == Kind::kAnyH;
   const bool split = kind == Kind::kSplit;
   if (split && a.T > ATTNRES_SPLIT_MAX_TOKENS) return ATTNRES_E_UNSUPPORTED;
@@ -1578,3 +1583,15 @@ extern "C" int attnres_device_status(int device) {
 }
 
 extern "C" int attnres_last_hip_error(void) { return g_last_hip.load(); }
+
+extern "C" int attnres_auto_path(int64_t T, int64_t H, int num_blocks) {
+  using namespace attnres;
+  if (T < 0 || T > kMaxTokens || H <= 0) return ATTNRES_E_SHAPE;
+  if (H % kSeg != 0 || H > kMaxHidden) return ATTNRES_E_UNSUPPORTED;
+  if (num_blocks < 0 || num_blocks > kMaxBlocks) return ATTNRES_E_NUM_BLOCKS;
+  switch (auto_choice(T, H, num_blocks)) {
+    case Kind::kSplit: return ATTNRES_PATH_SPLIT;
+    case Kind::kRow: return ATTNRES_PATH_ROW;
+    default: return ATTNRES_PATH_ANY_H;
+  }
+}

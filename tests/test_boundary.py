@@ -42,6 +42,36 @@ def test_library_exports_every_declared_symbol(A):
     assert not missing, f"symbols declared but not exported: {missing}"
 
 
+def test_automatic_kernel_choice(A):
+    """attnres_auto_path, the choice attnres_fwd makes, against the
+    documented rule.  At 7168: split up to 40/40/56/64/64/64/80/80 tokens
+    for 1..8 block rows, else the tuned row kernel, and row at every T with
+    no block rows.  Above 7168: split up to 48 tokens with block rows, else
+    the any-H kernel.  Below: the any-H kernel.  Host only."""
+    split_max = [None, 40, 40, 56, 64, 64, 64, 80, 80]
+    for nb in range(9):
+        for T in (0, 1, 2, 39, 40, 41, 48, 49, 56, 57, 64, 65, 80, 81, 256, 1024, 8192):
+            want = (A.ATTNRES_PATH_SPLIT if nb > 0 and T <= split_max[nb]
+                    else A.ATTNRES_PATH_ROW)
+            assert A.attnres_auto_path(T, 7168, nb) == want, (T, nb)
+    for H in (7176, 8192, 14344, 16384):
+        for nb in range(9):
+            for T in (1, 48, 49, 1024):
+                want = A.ATTNRES_PATH_SPLIT if nb > 0 and T <= 48 else A.ATTNRES_PATH_ANY_H
+                assert A.attnres_auto_path(T, H, nb) == want, (T, H, nb)
+    for H in (8, 2048, 4096, 7160):
+        for T in (1, 1024):
+            assert A.attnres_auto_path(T, H, 8) == A.ATTNRES_PATH_ANY_H
+    for (T, H, nb), err in (((1, 7170, 8), "ATTNRES_E_UNSUPPORTED"),
+                            ((1, 16392, 8), "ATTNRES_E_UNSUPPORTED"),
+                            ((1, 7168, 9), "ATTNRES_E_NUM_BLOCKS"),
+                            ((-1, 7168, 1), "ATTNRES_E_SHAPE"),
+                            ((1, 0, 1), "ATTNRES_E_SHAPE")):
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_auto_path(T, H, nb)
+        assert e.value.name == err
+
+
 def test_binding_status_table_matches_header(A):
     consts = _declared_constants()
     for name, code in consts.items():
