@@ -40,7 +40,8 @@ def _paths(T, H=7168):
 def _path_of(name):
     from kimi_k3_attention_amd import attnres as A
     return {"row": A.ATTNRES_PATH_ROW, "split": A.ATTNRES_PATH_SPLIT,
-            "any_h": A.ATTNRES_PATH_ANY_H, "any_h_large": A.ATTNRES_PATH_ANY_H}[name]
+            "any_h": A.ATTNRES_PATH_ANY_H, "any_h_large": A.ATTNRES_PATH_ANY_H,
+            "split_wide": A.ATTNRES_PATH_SPLIT}[name]
 
 
 # Rows over 8192 elements (four segments per lane, one workgroup per CU) at
@@ -666,7 +667,7 @@ def test_split_calls_from_two_threads(G):
     assert A.attnres_device_status() == A.ATTNRES_OK
 
 
-@pytest.mark.parametrize("path_name", ["row", "split", "any_h", "any_h_large"])
+@pytest.mark.parametrize("path_name", ["row", "split", "any_h", "any_h_large", "split_wide"])
 def test_graph_replay_matches_eager(G, path_name):
     """Calls captured in a hipGraph (torch.cuda.CUDAGraph) and replayed several
     times, with eager work and synchronisation in between, match the eager
@@ -678,6 +679,8 @@ def test_graph_replay_matches_eager(G, path_name):
     case = W.Case(f"graph_{path_name}", T=24, nb=6, widx=5, seed=70)
     if path_name == "any_h_large":
         case = W.other_hidden(16384, T=600, nb=6, seed=71)
+    if path_name == "split_wide":  # three segments per lane, matrix-core words
+        case = W.other_hidden(16384, T=5, nb=8, seed=72)
     inp = W.make_inputs(case)
     inp.delta[:] = 0
     d = G.upload(inp)
