@@ -918,8 +918,16 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   static_assert(NV <= kSlotYsq, "workspace slot too small");
   __shared__ __align__(16) float s_tr[NV][kTrStride];
 
-  const int64_t t = blockIdx.x / kParts;
-  const int part = blockIdx.x - int(t) * kParts;
+  // The dispatcher hands workgroup b to XCD b mod 8.  Token t's parts are
+  // workgroups 8 (kParts floor(t / 8) + part) + t mod 8, all on XCD t mod 8,
+  // so the exchanged words stay within one XCD's memory path (10 % off a
+  // single-token call).  Correctness does not rest on this placement: the
+  // exchange is agent-scope.  Workgroups past the last token exit at once.
+  const unsigned xcd = blockIdx.x & 7u, local = blockIdx.x >> 3;
+  const unsigned group = local / kParts;
+  const int part = int(local - group * kParts);
+  const int64_t t = int64_t(group) * 8 + xcd;
+  if (t >= p.T) return;
   const int lane = threadIdx.x;
   // Part `part` owns SPL segments per lane, part * 64 * SPL + lane + 64 i; at
   // H = 7168, one (512 elements per part).
@@ -1227,8 +1235,8 @@ bool cache_rewritten(const FwdArgs &a) {
 // 14 CUs (split) beats one CU per token (row) up to this many tokens, by
 // block count.  A single source (nb = 0) needs no exchange on the row path,
 // which is then faster at every T.
-constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 40, 56, 64, 64, 64, 80, 80};
-static_assert(80 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
+constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 56, 48, 64, 64, 72, 72, 72, 72};
+static_assert(72 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
 Kind auto_kind(int64_t T, int nb) {
   return nb > 0 && T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow;
 }
@@ -1452,7 +1460,9 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
     const int64_t cap = int64_t(cus) * wpc;
     if (a.T > cap) row_grid = unsigned(cap);
   }
-  const dim3 grid = split ? dim3(unsigned(a.T) * kParts) : dim3(row_grid);
+  // Split: 8 tokens per group of 8 kParts workgroups, placed per XCD (the
+  // kernel's token mapping).
+  const dim3 grid = split ? dim3(unsigned((a.T + 7) / 8) * 8 * kParts) : dim3(row_grid);
   const dim3 block = split ? dim3(kPartThreads) : dim3(kRowThreads);
   void *args[] = {&kp};
   e = hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, args, 0, s);

@@ -44,11 +44,11 @@ def test_library_exports_every_declared_symbol(A):
 
 def test_automatic_kernel_choice(A):
     """attnres_auto_path, the choice attnres_fwd makes, against the
-    documented rule.  At 7168: split up to 40/40/56/64/64/64/80/80 tokens
+    documented rule.  At 7168: split up to 56/48/64/64/72/72/72/72 tokens
     for 1..8 block rows, else the tuned row kernel, and row at every T with
     no block rows.  Above 7168: split up to 48 tokens with block rows, else
     the any-H kernel.  Below: the any-H kernel.  Host only."""
-    split_max = [None, 40, 40, 56, 64, 64, 64, 80, 80]
+    split_max = [None, 56, 48, 64, 64, 72, 72, 72, 72]
     for nb in range(9):
         for T in (0, 1, 2, 39, 40, 41, 48, 49, 56, 57, 64, 65, 80, 81, 256, 1024, 8192):
             want = (A.ATTNRES_PATH_SPLIT if nb > 0 and T <= split_max[nb]
