@@ -1241,15 +1241,20 @@ Kind auto_kind(int64_t T, int nb) {
   return nb > 0 && T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow;
 }
 // Above H = 7168 (2-3 segments per lane and part) the split path wins up to
-// about 48 tokens with 1-8 blocks; beyond, its parts hold too many registers
-// and the any-H row kernel is faster (H = 16384, nb = 8: T = 48 split 10.4
-// against 13.4 us, T = 80 17.9 against 14.0 us).
+// about 48 tokens with 1-8 blocks while H <= 8192, where the any-H row kernel
+// is relatively fast (H = 8192, nb = 8: T = 48 split 7.6 against 8.2 us,
+// T = 64 8.5 against 8.4), and up to 72 tokens beyond (H = 9216-16384, every
+// nb and T up to 72; H = 16384, nb = 8: T = 72 12.0 against 13.7 us, T = 80
+// 17.6 against 13.9).
 constexpr int kSplitMaxTWide = 48;
+constexpr int kSplitMaxTWider = 72;
+constexpr int64_t kWiderHidden = 8192;
 
 // The kernel attnres_fwd runs for T tokens, hidden size H and nb block rows.
 Kind auto_choice(int64_t T, int64_t H, int nb) {
   if (H == kHidden) return auto_kind(T, nb);
-  if (H > kHidden && nb > 0 && T <= kSplitMaxTWide) return Kind::kSplit;
+  if (H > kHidden && nb > 0 && T <= (H > kWiderHidden ? kSplitMaxTWider : kSplitMaxTWide))
+    return Kind::kSplit;
   return Kind::kAnyH;
 }
 

@@ -46,18 +46,19 @@ def test_automatic_kernel_choice(A):
     """attnres_auto_path, the choice attnres_fwd makes, against the
     documented rule.  At 7168: split up to 56/48/64/64/72/72/72/72 tokens
     for 1..8 block rows, else the tuned row kernel, and row at every T with
-    no block rows.  Above 7168: split up to 48 tokens with block rows, else
-    the any-H kernel.  Below: the any-H kernel.  Host only."""
+    no block rows.  Above 7168: split up to 48 tokens with block rows while
+    H <= 8192 and up to 72 beyond, else the any-H kernel.  Below: the any-H kernel.  Host only."""
     split_max = [None, 56, 48, 64, 64, 72, 72, 72, 72]
     for nb in range(9):
         for T in (0, 1, 2, 39, 40, 41, 48, 49, 56, 57, 64, 65, 80, 81, 256, 1024, 8192):
             want = (A.ATTNRES_PATH_SPLIT if nb > 0 and T <= split_max[nb]
                     else A.ATTNRES_PATH_ROW)
             assert A.attnres_auto_path(T, 7168, nb) == want, (T, nb)
-    for H in (7176, 8192, 14344, 16384):
+    for H in (7176, 8192, 8200, 14344, 16384):
         for nb in range(9):
-            for T in (1, 48, 49, 1024):
-                want = A.ATTNRES_PATH_SPLIT if nb > 0 and T <= 48 else A.ATTNRES_PATH_ANY_H
+            for T in (1, 48, 49, 72, 73, 1024):
+                limit = 48 if H <= 8192 else 72
+                want = A.ATTNRES_PATH_SPLIT if nb > 0 and T <= limit else A.ATTNRES_PATH_ANY_H
                 assert A.attnres_auto_path(T, H, nb) == want, (T, H, nb)
     for H in (8, 2048, 4096, 7160):
         for T in (1, 1024):

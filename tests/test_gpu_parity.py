@@ -182,7 +182,9 @@ HIDDEN_CASES = [
     dict(H=7160, T=20, nb=5),             # one segment short of 7168
     dict(H=8192, T=64, nb=8, has_delta=False),
     dict(H=8200, T=12, nb=2),             # first size with four segments per lane
+    dict(H=9216, T=72, nb=3),             # largest T the automatic choice splits
     dict(H=12288, T=48, nb=6),
+    dict(H=16384, T=73, nb=8, has_onorm=False),  # first T past it: any-H
     dict(H=16376, T=10, nb=8),            # 2047 segments: masked, 8 waves
     dict(H=16384, T=24, nb=8, widx=0),
 ]
