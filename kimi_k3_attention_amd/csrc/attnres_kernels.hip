@@ -1158,17 +1158,22 @@ KernelFn split_fn(bool d, bool o) {
 // The split path above 7168: SPL segments per lane per part, masked at the
 // row end.
 template <int NB, int SPL>
-KernelFn split_wide_fn(bool d, bool o) {
+KernelFn split_masked_fn(bool d, bool o) {
   if (d)
     return o ? attnres_split_kernel<NB, true, true, SPL, true>
              : attnres_split_kernel<NB, true, false, SPL, true>;
   return o ? attnres_split_kernel<NB, false, true, SPL, true>
            : attnres_split_kernel<NB, false, false, SPL, true>;
 }
-KernelFn pick_split_wide(int nb, bool d, bool o, int spl) {
+// The split kernel at H != 7168: SPL segments per lane and part, masked at
+// the row end (SPL = 1 below 7168, 2 or 3 above).
+KernelFn pick_split_masked(int nb, bool d, bool o, int spl) {
   switch (nb) {
-#define ATTNRES_CASE(N) \
-  case N: return spl == 2 ? split_wide_fn<N, 2>(d, o) : split_wide_fn<N, 3>(d, o);
+#define ATTNRES_CASE(N)                                                     \
+  case N:                                                                   \
+    return spl == 1   ? split_masked_fn<N, 1>(d, o)                         \
+           : spl == 2 ? split_masked_fn<N, 2>(d, o)                         \
+                      : split_masked_fn<N, 3>(d, o);
     ATTNRES_CASE(0) ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
     ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
 #undef ATTNRES_CASE
@@ -1249,11 +1254,23 @@ Kind auto_kind(int64_t T, int nb) {
 constexpr int kSplitMaxTWide = 48;
 constexpr int kSplitMaxTWider = 72;
 constexpr int64_t kWiderHidden = 8192;
+// Below H = 7168 (one masked segment per lane and part) the any-H row kernel
+// is faster at H <= 3072; the split path leads from H = 5120 with 1-8 blocks
+// up to 48 tokens (H = 6144, nb = 8, T = 48: 6.5 against 7.5 us) and at
+// H = 4096 with 8 blocks up to 32 (5.4 against 5.6 us; with 4 blocks a tie).
+constexpr int64_t kNarrowSplitHidden = 5120;
+constexpr int kSplitMaxTNarrow = 48;
+constexpr int64_t kNarrowSplitHiddenFull = 4096;
+constexpr int kSplitMaxTNarrowFull = 32;
 
 // The kernel attnres_fwd runs for T tokens, hidden size H and nb block rows.
 Kind auto_choice(int64_t T, int64_t H, int nb) {
   if (H == kHidden) return auto_kind(T, nb);
   if (H > kHidden && nb > 0 && T <= (H > kWiderHidden ? kSplitMaxTWider : kSplitMaxTWide))
+    return Kind::kSplit;
+  if (H < kHidden && nb > 0 && H >= kNarrowSplitHidden && T <= kSplitMaxTNarrow)
+    return Kind::kSplit;
+  if (H < kHidden && nb == kMaxBlocks && H >= kNarrowSplitHiddenFull && T <= kSplitMaxTNarrowFull)
     return Kind::kSplit;
   return Kind::kAnyH;
 }
@@ -1363,13 +1380,13 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   if (a.T == 0) return ATTNRES_OK;
 
   // The tuned kernels are built for H = 7168; every other H runs the any-H
-  // row kernel, which can also be forced at 7168.  Above 7168 the split path
-  // also runs, its 14 parts taking 2 or 3 segments per lane (masked at the
-  // row end), and the automatic choice uses it for the same small batches.
+  // row kernel, which can also be forced at 7168.  The split path runs at
+  // every H: away from 7168 its 14 parts take 1 (below), 2 or 3 (above)
+  // segments per lane, masked at the row end, and above 7168 the automatic
+  // choice uses it for small batches.
   const bool tuned = a.H == kHidden;
   const bool wide = a.H > kHidden;
   const int split_spl = wide ? int((a.H / kSeg + kParts * kPartThreads - 1) / (kParts * kPartThreads)) : 1;
-  if (path == ATTNRES_PATH_SPLIT && !tuned && !wide) return ATTNRES_E_UNSUPPORTED;
   Kind kind;
   if (path == ATTNRES_PATH_ANY_H)
     kind = Kind::kAnyH;
@@ -1453,7 +1470,7 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
   // tokens: T = 1024, nb = 8, with a delta: 33.7 -> 32.6 us, T = 4096:
   // 131 -> 117 us.  Smaller calls (latency-bound) read them streaming.
   const bool cache_rw = kind == Kind::kRow && cache_rewritten(a);
-  KernelFn fn = split && wide ? pick_split_wide(a.num_blocks, has_d, has_o, split_spl)
+  KernelFn fn = split && !tuned ? pick_split_masked(a.num_blocks, has_d, has_o, split_spl)
                               : pick(kind, a.num_blocks, has_d, has_o, cache_rw);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;
   unsigned row_grid = unsigned(a.T);

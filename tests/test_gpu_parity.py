@@ -28,11 +28,11 @@ def _paths(T, H=7168):
     """Every kernel that can run a call of T tokens at hidden size H: at 7168
     the tuned row kernel, the split kernel (T <= 256) and the any-H kernel;
     at other sizes the any-H kernel (through the automatic choice, the row
-    selector and its own), and above 7168 also the split kernel with 2 or 3
-    segments per lane (T <= 256)."""
+    selector and its own) and the split kernel with 1 (below 7168), 2 or 3
+    segments per lane, masked (T <= 256)."""
     from kimi_k3_attention_amd import attnres as A
     ps = [None, A.ATTNRES_PATH_ROW, A.ATTNRES_PATH_ANY_H]
-    if H >= 7168 and T <= A.ATTNRES_SPLIT_MAX_TOKENS:
+    if T <= A.ATTNRES_SPLIT_MAX_TOKENS:
         ps.append(A.ATTNRES_PATH_SPLIT)
     return ps
 
@@ -174,11 +174,14 @@ def test_variant_matrix(G, case):
 # per lane, rows that fill whole waves exactly and rows that need masking.
 HIDDEN_CASES = [
     dict(H=8, T=9, nb=3),                 # one segment per row: 63 masked lanes
+    dict(H=64, T=3, nb=8),                # split: 13 of 14 parts wholly masked
     dict(H=1024, T=33, nb=8),
     dict(H=2048, T=300, nb=4, has_onorm=False),
     dict(H=2880, T=40, nb=7),             # 360 segments: masked, 3 waves
     dict(H=4096, T=129, nb=8, widx=-1),
+    dict(H=4096, T=32, nb=8, has_delta=False),  # automatic choice: split below 7168
     dict(H=5120, T=17, nb=0),
+    dict(H=6144, T=48, nb=5),
     dict(H=7160, T=20, nb=5),             # one segment short of 7168
     dict(H=8192, T=64, nb=8, has_delta=False),
     dict(H=8200, T=12, nb=2),             # first size with four segments per lane
@@ -225,20 +228,6 @@ def test_large_rows_back_to_back(G):
             G.say("large rows back to back, repetition", rep, "call", k)
             G.check_full(inps[k], G.download(d), refs[k])
     assert A.attnres_device_status() == A.ATTNRES_OK
-
-
-def test_split_path_refuses_smaller_hidden_sizes(G):
-    """The split path runs at 7168 and above; below, forcing it is an error
-    that touches nothing."""
-    from kimi_k3_attention_amd import attnres as A
-    case = W.other_hidden(4096, T=4, nb=2)
-    inp = W.make_inputs(case)
-    d = G.upload(inp)
-    with pytest.raises(A.AttnResError) as e:
-        G.run(d, path=A.ATTNRES_PATH_SPLIT)
-    assert e.value.name == "ATTNRES_E_UNSUPPORTED"
-    got = G.download(d)
-    assert (got.out == inp.out_init).all() and (got.prefix == inp.prefix).all()
 
 
 @pytest.mark.parametrize("H,T,nb", [(7168, 37, 5), (7168, 200, 8), (7168, 1, 8), (2880, 50, 4),
