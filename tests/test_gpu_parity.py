@@ -323,7 +323,7 @@ def _random_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", _random_cases(40, 1) + _random_cases(80, 2) + _random_cases(150, 4),
+@pytest.mark.parametrize("case", _random_cases(40, 1) + _random_cases(80, 2) + _random_cases(150, 4) + _random_cases(150, 8),
                          ids=lambda c: c.name)
 def test_random_configuration(G, case):
     _run_and_check_all_paths(G, case)
