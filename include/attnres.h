@@ -72,9 +72,9 @@ extern "C" {
                                 -/56/48/64/64/72/72/72/72 with 0..8 blocks (never with
                                 0 blocks), else row; above 7168 split with 1..8 blocks
                                 for T <= 48 up to H = 8192 and for T <= 72 beyond,
-                                else any-H; below 7168 split for T <= 48 with 1..8
-                                blocks from H = 5120 and for T <= 32 with 8 blocks
-                                from H = 4096, else any-H */
+                                else any-H; below 7168 split above H = 4096 for
+                                T <= 48 with 1..8 blocks, at H = 4096 for T <= 32
+                                with 7..8 blocks and T <= 16 with 5..6, else any-H */
 #define ATTNRES_PATH_ROW 1   /* one workgroup per token (the any-H kernel when H != 7168) */
 #define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (any H,
                                 T <= 256) */

@@ -1255,22 +1255,25 @@ constexpr int kSplitMaxTWide = 48;
 constexpr int kSplitMaxTWider = 72;
 constexpr int64_t kWiderHidden = 8192;
 // Below H = 7168 (one masked segment per lane and part) the any-H row kernel
-// is faster at H <= 3072; the split path leads from H = 5120 with 1-8 blocks
-// up to 48 tokens (H = 6144, nb = 8, T = 48: 6.5 against 7.5 us) and at
-// H = 4096 with 8 blocks up to 32 (5.4 against 5.6 us; with 4 blocks a tie).
-constexpr int64_t kNarrowSplitHidden = 5120;
+// is faster at H <= 3072.  Above 4096 the split path leads with 1-8 blocks up
+// to 48 tokens (H = 4608, nb = 4, T = 48: 5.0 against 6.0 us; H = 6144,
+// nb = 8: 6.5 against 7.5).  At 4096, which suits the any-H kernel, it leads
+// with 7-8 blocks up to 32 tokens and with 5-6 up to 16 (nb = 8, T = 32: 5.4
+// against 5.6 us; nb = 6, T = 32: a tie; nb = 4: a tie up to T = 16).
+constexpr int64_t kNarrowSplitHidden = 4096;
 constexpr int kSplitMaxTNarrow = 48;
-constexpr int64_t kNarrowSplitHiddenFull = 4096;
-constexpr int kSplitMaxTNarrowFull = 32;
+constexpr int kSplitMaxTNarrow7 = 32;   // at 4096 with 7 or 8 blocks
+constexpr int kSplitMaxTNarrow5 = 16;   // at 4096 with 5 or 6 blocks
 
 // The kernel attnres_fwd runs for T tokens, hidden size H and nb block rows.
 Kind auto_choice(int64_t T, int64_t H, int nb) {
   if (H == kHidden) return auto_kind(T, nb);
   if (H > kHidden && nb > 0 && T <= (H > kWiderHidden ? kSplitMaxTWider : kSplitMaxTWide))
     return Kind::kSplit;
-  if (H < kHidden && nb > 0 && H >= kNarrowSplitHidden && T <= kSplitMaxTNarrow)
+  if (H < kHidden && H > kNarrowSplitHidden && nb > 0 && T <= kSplitMaxTNarrow)
     return Kind::kSplit;
-  if (H < kHidden && nb == kMaxBlocks && H >= kNarrowSplitHiddenFull && T <= kSplitMaxTNarrowFull)
+  if (H == kNarrowSplitHidden &&
+      ((nb >= 7 && T <= kSplitMaxTNarrow7) || (nb >= 5 && T <= kSplitMaxTNarrow5)))
     return Kind::kSplit;
   return Kind::kAnyH;
 }
