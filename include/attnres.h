@@ -74,7 +74,9 @@ extern "C" {
                                 for T <= 48 up to H = 8192 and for T <= 72 beyond,
                                 else any-H; below 7168 split above H = 4096 for
                                 T <= 48 with 1..8 blocks, at H = 4096 for T <= 32
-                                with 7..8 blocks and T <= 16 with 5..6, else any-H */
+                                with 7..8 blocks and T <= 16 with 5..6, from 2560 to
+                                below 4096 (not multiples of 1024) for T <= 16 with
+                                1..8 blocks, else any-H */
 #define ATTNRES_PATH_ROW 1   /* one workgroup per token (the any-H kernel when H != 7168) */
 #define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (any H,
                                 T <= 256) */

@@ -1264,6 +1264,12 @@ constexpr int64_t kNarrowSplitHidden = 4096;
 constexpr int kSplitMaxTNarrow = 48;
 constexpr int kSplitMaxTNarrow7 = 32;   // at 4096 with 7 or 8 blocks
 constexpr int kSplitMaxTNarrow5 = 16;   // at 4096 with 5 or 6 blocks
+// From 2560 up to 4096 the any-H kernel is strong at the multiples of 1024
+// (3072: ahead at nb = 1 and 4) and weaker between them, where the split path
+// leads or ties up to 16 tokens at every block count (H = 3584, nb = 8,
+// T = 1: 4.5 against 5.6 us; H = 2560, nb = 1, T = 16: a tie).
+constexpr int64_t kOddSplitHidden = 2560;
+constexpr int kSplitMaxTOdd = 16;
 
 // The kernel attnres_fwd runs for T tokens, hidden size H and nb block rows.
 Kind auto_choice(int64_t T, int64_t H, int nb) {
@@ -1274,6 +1280,9 @@ Kind auto_choice(int64_t T, int64_t H, int nb) {
     return Kind::kSplit;
   if (H == kNarrowSplitHidden &&
       ((nb >= 7 && T <= kSplitMaxTNarrow7) || (nb >= 5 && T <= kSplitMaxTNarrow5)))
+    return Kind::kSplit;
+  if (H >= kOddSplitHidden && H < kNarrowSplitHidden && H % 1024 != 0 && nb > 0 &&
+      T <= kSplitMaxTOdd)
     return Kind::kSplit;
   return Kind::kAnyH;
 }

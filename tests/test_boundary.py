@@ -49,7 +49,8 @@ def test_automatic_kernel_choice(A):
     no block rows.  Above 7168: split up to 48 tokens with block rows while
     H <= 8192 and up to 72 beyond, else the any-H kernel.  Below: split up to
     48 tokens with block rows above H = 4096; at 4096 up to 32 with 7-8
-    block rows and up to 16 with 5-6; else the any-H kernel.  Host only."""
+    block rows and up to 16 with 5-6; from 2560 to below 4096, except at
+    multiples of 1024, up to 16 with block rows; else the any-H kernel.  Host only."""
     split_max = [None, 56, 48, 64, 64, 72, 72, 72, 72]
     for nb in range(9):
         for T in (0, 1, 2, 39, 40, 41, 48, 49, 56, 57, 64, 65, 80, 81, 256, 1024, 8192):
@@ -62,11 +63,12 @@ def test_automatic_kernel_choice(A):
                 limit = 48 if H <= 8192 else 72
                 want = A.ATTNRES_PATH_SPLIT if nb > 0 and T <= limit else A.ATTNRES_PATH_ANY_H
                 assert A.attnres_auto_path(T, H, nb) == want, (T, H, nb)
-    for H in (8, 2048, 3072, 4088, 4096, 4104, 5120, 7160):
+    for H in (8, 2048, 2552, 2560, 3072, 3584, 4088, 4096, 4104, 5120, 7160):
         for nb in range(9):
             for T in (1, 16, 17, 32, 33, 48, 49, 1024):
                 split = nb > 0 and ((H > 4096 and T <= 48) or
-                                    (H == 4096 and ((nb >= 7 and T <= 32) or (nb >= 5 and T <= 16))))
+                                    (H == 4096 and ((nb >= 7 and T <= 32) or (nb >= 5 and T <= 16))) or
+                                    (2560 <= H < 4096 and H % 1024 != 0 and T <= 16))
                 want = A.ATTNRES_PATH_SPLIT if split else A.ATTNRES_PATH_ANY_H
                 assert A.attnres_auto_path(T, H, nb) == want, (T, H, nb)
     for (T, H, nb), err in (((1, 7170, 8), "ATTNRES_E_UNSUPPORTED"),

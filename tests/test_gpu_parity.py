@@ -181,6 +181,7 @@ HIDDEN_CASES = [
     dict(H=4096, T=129, nb=8, widx=-1),
     dict(H=4096, T=32, nb=8, has_delta=False),  # automatic choice: split below 7168
     dict(H=4608, T=48, nb=2),
+    dict(H=3584, T=16, nb=1),
     dict(H=5120, T=17, nb=0),
     dict(H=6144, T=48, nb=5),
     dict(H=7160, T=20, nb=5),             # one segment short of 7168
