@@ -44,6 +44,10 @@ DOMINANT_KERNEL = "attnres_row_kernel<8, true, true, true>"
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "attnres_row_kernel_mid_prefill_T1024_traffic.json")
 CALIBRATION_BYTES = 512 << 20
+# Calls per timed sample of the headline and of the traffic probe: enough
+# that the fixed start-up cost of a graph replay (~50 us) is under 0.3 % of
+# the sample at any --steps.
+MIN_TIMED_CALLS = 600
 KERNEL_SOURCES = [os.path.join(ROOT, "kimi_k3_attention_amd", "csrc", f)
                   for f in ("attnres_kernels.hip", "attnres_internal.h")]
 
@@ -95,10 +99,15 @@ class Set:
                           c.widx, self.out[sl], path=path)
 
 
-def time_graph(calls, steps: int, replays: int = 1, warm: int = 1):
+def time_graph(calls, steps: int, replays: int = 1, warm: int = 1, min_calls: int = 0):
     """Captures `steps` calls (cycling over `calls`) into one hipGraph and
-    returns the elapsed ms of each replay (hipEvents on the launch stream),
-    after `warm` untimed replays (graph upload, first touch of the buffers)."""
+    returns, for each of `replays` timed samples, the elapsed ms per graph
+    replay, after `warm` untimed replays (graph upload, first touch of the
+    buffers).  A sample replays the graph R = ceil(min_calls / steps) times
+    back to back between one pair of hipEvents on the launch stream, with no
+    host synchronisation inside, so the graph's fixed start-up cost is spread
+    over at least `min_calls` calls whatever `steps` is; the sample's time is
+    divided by R."""
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
@@ -108,6 +117,7 @@ def time_graph(calls, steps: int, replays: int = 1, warm: int = 1):
     for _ in range(warm):
         g.replay()
     torch.cuda.synchronize()
+    reps = graph_repeats(steps, min_calls)
     times = []
     stream = torch.cuda.current_stream()
     for _ in range(replays):
@@ -115,12 +125,18 @@ def time_graph(calls, steps: int, replays: int = 1, warm: int = 1):
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        g.replay()
+        for _ in range(reps):
+            g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
+        times.append(e0.elapsed_time(e1) / reps)
     del g
     return times
+
+
+def graph_repeats(steps: int, min_calls: int) -> int:
+    """The R that time_graph uses: graph replays per timed sample."""
+    return max(1, -(-min_calls // steps))
 
 
 def time_eager(calls, steps: int):
@@ -166,18 +182,22 @@ def bench_mid(steps: int, warmup: int, eager: bool):
         ms = time_eager(calls, steps)
         reps = [ms]
     else:
-        # Six replays, each timing exactly `steps` calls, after three untimed
-        # ones (the first ~20 ms after building the inputs run a few percent
-        # slow); the median is reported.
-        reps = time_graph(calls, steps, replays=6, warm=3)
+        # Six timed samples after three untimed replays (the first ~20 ms
+        # after building the inputs run a few percent slow).  The graph holds
+        # exactly `steps` calls; each sample replays it back to back until it
+        # covers at least MIN_TIMED_CALLS calls, so the graph's start-up cost
+        # does not depend on `steps`.  The median sample is reported.
+        reps = time_graph(calls, steps, replays=6, warm=3, min_calls=MIN_TIMED_CALLS)
         ms = pct(reps, 50)
+    repeats = 1 if eager else graph_repeats(steps, MIN_TIMED_CALLS)
     per_call_ms = ms / steps
     per_call = [r / steps * 1e3 for r in reps]
     gbps = per_call_bytes / (per_call_ms * 1e-3) / 1e9
-    log(f"mid prefill: {per_call_ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+    log(f"mid prefill: {per_call_ms * 1e3:.2f} us/call, {gbps:.0f} GB/s "
+        f"({repeats} x {steps} calls per timed sample)")
     return dict(case=case, sets=sets, per_call_ms=per_call_ms, gbps=gbps, bytes=per_call_bytes,
                 us=dict(p20=pct(per_call, 20), p50=pct(per_call, 50), p80=pct(per_call, 80)),
-                nsets=nsets)
+                nsets=nsets, calls_timed=repeats * steps, graph_repeats=repeats)
 
 
 def bench_decode(steps: int):
@@ -444,7 +464,7 @@ def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168):
         for fn in calls:
             fn()
         torch.cuda.synchronize()
-        t = time_graph(calls, steps, replays=3)
+        t = time_graph(calls, steps, replays=3, min_calls=MIN_TIMED_CALLS)
         us = pct([x / steps * 1e3 for x in t], 50)
         nbytes = 2 * H * T * 13
         res[name] = dict(T=T, us=round(us, 2), GBps=round(nbytes / us / 1e3, 1),
@@ -473,7 +493,7 @@ def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168):
         for fn in calls:
             fn()
         torch.cuda.synchronize()
-        t = time_graph(calls, steps, replays=3)
+        t = time_graph(calls, steps, replays=3, min_calls=MIN_TIMED_CALLS)
         us = pct([x / steps * 1e3 for x in t], 50)
         nbytes = 2 * H * T * (reads + wd + wi)
         res[name] = dict(T=T, us=round(us, 2), GBps=round(nbytes / us / 1e3, 1),
@@ -553,6 +573,16 @@ def cpu_baseline(single_s: float = 8.0, multi_s: float = 1.5):
                 ms_per_call=round(dtn * 1e3, 1), host=_host_cpu())
 
 
+def kernel_trace_entry(nbytes: int):
+    """The kernel-only figure from the committed rocprofv3 trace, labelled."""
+    us = load_kernel_trace_us()
+    if us is None:
+        return None
+    gbps = nbytes / us / 1e3
+    return {"source": os.path.relpath(KERNEL_STATS_FILE, ROOT), "average_us": us,
+            "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def load_traffic():
     """HBM bytes per launch from the committed counter runs, if they were taken
     on the current kernel source."""
@@ -563,6 +593,26 @@ def load_traffic():
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+KERNEL_STATS_FILE = os.path.join(PROFILES, "attnres_row_kernel_mid_prefill_T1024_kernel_stats.txt")
+
+
+def load_kernel_trace_us():
+    """The dominant kernel's average duration (us) in the committed rocprofv3
+    kernel-trace summary of the headline command, if that summary was taken
+    on the current kernel source."""
+    if not os.path.exists(KERNEL_STATS_FILE):
+        return None
+    with open(KERNEL_STATS_FILE) as f:
+        lines = f.read().splitlines()
+    if not any(l.startswith("# kernel source hash: " + kernel_source_hash()) for l in lines):
+        return None
+    for l in lines:
+        parts = [x.strip() for x in l.split("|")]
+        if len(parts) == 7 and parts[0] == DOMINANT_KERNEL:
+            return float(parts[5])  # the per-dispatch trace's average
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -780,8 +830,14 @@ def main():
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBPS, 4),
                          "traffic": load_traffic(),
-                         "algorithmic_bytes_per_launch": mid["bytes"]},
+                         "algorithmic_bytes_per_launch": mid["bytes"],
+                         "achieved_from": "per-call time of back-to-back graph replays on the "
+                                          "launch stream (hipEvents), kernels plus the gaps "
+                                          "between them",
+                         "kernel_trace": kernel_trace_entry(mid["bytes"])},
             "mid_prefill_us_per_call": {k: round(v, 3) for k, v in mid["us"].items()},
+            "calls_timed": mid["calls_timed"],
+            "graph_repeats": mid["graph_repeats"],
         })
     if decode is not None:
         line["decode_T1_us_per_call"] = {k: round(v["cold_us"], 3) for k, v in decode.items()}

@@ -111,6 +111,45 @@ def oracle_full(inp: W.Inputs):
                                  c.cap, c.nb, inp.res_w, inp.rms_w, c.eps, inp.onw, c.oeps, c.widx)
 
 
+def oracle_full_threaded(inp: W.Inputs, threads: int = 16):
+    """The oracle over every token of the call, run as contiguous token ranges
+    on a pool of threads (tokens are independent; the C oracle runs without
+    the GIL).  Returns out_bits, prefix_after and bank_after of the whole call,
+    stitched from the ranges; the ranges' bank slices are disjoint because a
+    token's rows lie within its token stride."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    c = inp.case
+    T, ts = c.T, c.token_stride
+    n = max(1, min(threads, T))
+    bounds = [(T * k // n, T * (k + 1) // n) for k in range(n)]
+    bank_after = inp.bank.copy()
+    out_bits = np.empty((T, c.H), dtype=np.uint16)
+    prefix_after = np.empty((T, c.H), dtype=np.uint16)
+
+    def run(ab):
+        a, b = ab
+        if a == b:
+            return
+        r = oracle.attnres_oracle(inp.prefix[a:b], None if inp.delta is None else inp.delta[a:b],
+                                  inp.bank[a * ts:b * ts], ts, c.slot_stride, c.cap, c.nb,
+                                  inp.res_w, inp.rms_w, c.eps, inp.onw, c.oeps, c.widx)
+        out_bits[a:b] = r.out_bits
+        prefix_after[a:b] = r.prefix_after
+        bank_after[a * ts:b * ts] = r.bank_after
+
+    with ThreadPoolExecutor(max_workers=n) as pool:
+        list(pool.map(run, bounds))
+    return FullRef(out_bits, prefix_after, bank_after)
+
+
+@dataclass
+class FullRef:
+    out_bits: np.ndarray
+    prefix_after: np.ndarray
+    bank_after: np.ndarray
+
+
 def oracle_sample(inp: W.Inputs, tokens: Sequence[int]):
     import oracle
     c = inp.case

@@ -110,3 +110,28 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_graph_repeats_cover_the_minimum_calls():
+    # The driver's --steps 20 and the default 300 both time >= MIN_TIMED_CALLS calls.
+    for steps in (1, 20, 300, 599, 600, 601, 5000):
+        r = bench.graph_repeats(steps, bench.MIN_TIMED_CALLS)
+        assert r * steps >= bench.MIN_TIMED_CALLS
+        assert (r - 1) * steps < bench.MIN_TIMED_CALLS
+    assert bench.graph_repeats(20, 0) == 1
+
+
+def test_kernel_trace_average_read_only_for_current_source(profiles_dir, monkeypatch):
+    f = profiles_dir / "stats.txt"
+    monkeypatch.setattr(bench, "KERNEL_STATS_FILE", str(f))
+    os.makedirs(profiles_dir)
+    body = ["# rocprofv3 kernel statistics, x", "# command: c",
+            f"# kernel source hash: {bench.kernel_source_hash()}",
+            f"{bench.DOMINANT_KERNEL} | 448 | 458752 | 0 | 2720 | 32.902 | 32.557"]
+    f.write_text("\n".join(body) + "\n")
+    assert bench.load_kernel_trace_us() == pytest.approx(32.902)
+    e = bench.kernel_trace_entry(190883840)
+    assert e["frac"] == pytest.approx(190883840 / 32.902 / 1e3 / bench.HBM_PEAK_GBPS, abs=1e-4)
+    body[2] = "# kernel source hash: other"
+    f.write_text("\n".join(body) + "\n")
+    assert bench.load_kernel_trace_us() is None
