@@ -56,11 +56,25 @@ def log(*msg):
     print("[bench]", *msg, file=sys.stderr, flush=True)
 
 
+# The kernels' device code ends where the launch layer begins; host-only
+# changes below this line (entry points, workspace handling) leave the
+# measured kernels, hence their committed counters, valid.
+DEVICE_CODE_END = b"// specialisation tables"
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernels' device code: the kernel source up to the launch
+    layer, and the internal header."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(f, "rb") as fh:
-            h.update(fh.read())
+            text = fh.read()
+        if f.endswith(".hip"):
+            end = text.find(DEVICE_CODE_END)
+            if end < 0:
+                raise RuntimeError(f"{f}: no '{DEVICE_CODE_END.decode()}' marker")
+            text = text[:end]
+        h.update(text)
     return h.hexdigest()[:16]
 
 
