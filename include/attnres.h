@@ -169,6 +169,36 @@ int attnres_fwd_strided(void *prefix, int64_t prefix_stride,
                         int block_write_idx, void *out, int64_t out_stride,
                         int64_t T, int64_t H, void *stream, int path);
 
+/*
+ * attnres_fwd_noalloc -- attnres_fwd_strided for callers that cannot allocate
+ * device memory: code under hipGraph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results and checks as
+ * attnres_fwd_strided; it never calls hipMalloc, hipFree or any allocating
+ * routine.  The only kernel that needs memory beyond the arguments is the
+ * split path's (its cross-workgroup exchange words and fault flag).  This
+ * entry point gives it a static device array of 1,835,264 bytes per device
+ * (ATTNRES_SPLIT_MAX_TOKENS tokens), held until the process ends, instead of
+ * the allocated workspace.  A split-path call of more than
+ * ATTNRES_SPLIT_MAX_TOKENS tokens is rejected with ATTNRES_E_UNSUPPORTED
+ * before any GPU work.  The array's device address is taken, and the array
+ * cleared, once per device: in attnres_init(device), or else at the first
+ * split-path call on that device outside graph capture (a call that needs it
+ * inside capture before that returns ATTNRES_E_NOT_INIT).  Nothing needs
+ * clearing between calls: the exchange words carry their own generation tags,
+ * and attnres_device_status reads and clears this array's fault flag too.
+ * Every call on a device shares that device's array, and calls are not
+ * ordered against each other: split-path calls that overlap on one GPU race
+ * (their results are not valid, and the bounded wait may give up).
+ */
+int attnres_fwd_noalloc(void *prefix, int64_t prefix_stride,
+                        const void *delta, int64_t delta_stride, void *blocks,
+                        int64_t block_token_stride, int64_t block_slot_stride,
+                        int max_blocks, int num_blocks,
+                        const void *res_w, const void *rms_w, float rms_eps,
+                        const void *output_norm_weight, float output_norm_eps,
+                        int block_write_idx, void *out, int64_t out_stride,
+                        int64_t T, int64_t H, void *stream, int path);
+
 /* The host-side argument checks of attnres_fwd, alone.  Makes no HIP call and
  * dereferences no pointer, so it runs without a GPU. */
 int attnres_validate(const void *prefix, const void *delta, const void *blocks,
@@ -189,16 +219,18 @@ int attnres_validate_strided(const void *prefix, int64_t prefix_stride,
                              int64_t T, int64_t H);
 
 /* Allocates and clears the split path's workspace on `device` (about 1.8 MB:
- * tagged partial-sum words and a fault flag).  Idempotent.
+ * tagged partial-sum words and a fault flag), and takes the address of (and
+ * clears) attnres_fwd_noalloc's static array there.  Idempotent.
  * Call it outside stream capture. */
 int attnres_init(int device);
 
 /* Frees every device's workspace.  No call may be in flight. */
 void attnres_shutdown(void);
 
-/* Reads (synchronously) and clears the split path's device fault flag on
- * `device`: ATTNRES_E_DEVICE_WAIT if a cross-workgroup wait ever gave up since
- * the last check (the counters are then reset), else ATTNRES_OK. */
+/* Reads (synchronously) and clears the split path's device fault flags on
+ * `device` (the allocated workspace's and attnres_fwd_noalloc's):
+ * ATTNRES_E_DEVICE_WAIT if a cross-workgroup wait ever gave up since the last
+ * check (the exchange words are then reset), else ATTNRES_OK. */
 int attnres_device_status(int device);
 
 /* Static description of a status code. */

@@ -60,6 +60,8 @@ _STRIDED_ARGS = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _int, _int, _vp, _vp, _f
                  _int, _vp, _i64, _i64, _i64]
 _lib.attnres_fwd_strided.argtypes = _STRIDED_ARGS + [_vp, _int]
 _lib.attnres_fwd_strided.restype = _int
+_lib.attnres_fwd_noalloc.argtypes = _STRIDED_ARGS + [_vp, _int]
+_lib.attnres_fwd_noalloc.restype = _int
 _lib.attnres_validate_strided.argtypes = list(_STRIDED_ARGS)
 _lib.attnres_validate_strided.restype = _int
 _lib.attnres_init.argtypes = [_int]
@@ -200,6 +202,34 @@ def attnres_fwd(prefix: torch.Tensor, delta: Optional[torch.Tensor],
             where = "attnres_fwd_path"
     if rc != ATTNRES_OK:
         raise AttnResError(rc, where)
+
+
+def attnres_fwd_noalloc(prefix: torch.Tensor, delta: Optional[torch.Tensor],
+                        blocks: Optional[torch.Tensor], num_blocks: int, res_w: torch.Tensor,
+                        rms_w: torch.Tensor, rms_eps: float,
+                        output_norm_weight: Optional[torch.Tensor], output_norm_eps: float,
+                        block_write_idx: int, out: torch.Tensor,
+                        stream: Optional[torch.cuda.Stream] = None,
+                        path: Optional[int] = None) -> None:
+    """attnres_fwd through the library's entry point that allocates nothing
+    (the split path then exchanges through a static per-device array; calls
+    that overlap on one GPU race).  Same arguments as attnres_fwd."""
+    m = _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
+                 output_norm_eps, block_write_idx, out)
+    dev = prefix.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for name, t in (("delta", delta), ("blocks", blocks), ("res_w", res_w), ("rms_w", rms_w),
+                    ("output_norm_weight", output_norm_weight), ("out", out)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, prefix on {dev}: all tensors must be "
+                             "on the same GPU")
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = _lib.attnres_fwd_noalloc(*_strided_args(m), s.cuda_stream,
+                                      ATTNRES_PATH_AUTO if path is None else int(path))
+    if rc != ATTNRES_OK:
+        raise AttnResError(rc, "attnres_fwd_noalloc")
 
 
 def attnres_fwd_path(*args, path: int, **kw) -> None:

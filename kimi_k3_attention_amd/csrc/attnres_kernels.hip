@@ -1325,6 +1325,24 @@ DeviceWorkspace g_ws[kMaxDevices];
 std::mutex g_ws_mu;
 std::atomic<int> g_last_hip{0};
 
+}  // namespace
+
+// The split path's workspace for attnres_fwd_noalloc, in static device
+// memory so that this entry point never allocates: the tagged words of
+// ATTNRES_SPLIT_MAX_TOKENS tokens, then the fault flag, laid out as in the
+// allocated workspace.  Each device that runs the library holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is taken once per device with
+// hipGetSymbolAddress (static_scratch_locked below), and only that address
+// is ever passed to a kernel or to a HIP memory call.
+constexpr size_t kScratchWords = kWorkspaceBytes / sizeof(uint64_t);
+static_assert(kScratchWords * sizeof(uint64_t) == kWorkspaceBytes, "scratch layout");
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+
+namespace {
+
+void *g_scratch[kMaxDevices];  // scratch's address on each device (under g_ws_mu)
+
 // Records a failed HIP call's error for attnres_last_hip_error and clears the
 // runtime's last-error state, so that the caller's next unrelated error check
 // does not report it again (the call has already returned ATTNRES_E_HIP).
@@ -1360,6 +1378,26 @@ int init_device_locked(int device) {
   return ATTNRES_OK;
 }
 
+// Takes scratch's address on `device` (with that device current) the first
+// time, and clears it then: the generation tags of a token's parts must agree
+// and the fault flag must start at zero.  Synchronous; outside graph capture.
+int static_scratch_locked(int device) {
+  if (g_scratch[device]) return ATTNRES_OK;
+  int prev = 0;
+  hipError_t e = hipGetDevice(&prev);
+  if (e != hipSuccess) return hip_fail(e);
+  if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e);
+  void *ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e == hipSuccess && ptr == nullptr) e = hipErrorInvalidSymbol;
+  if (e == hipSuccess) e = hipMemset(ptr, 0, kWorkspaceBytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) return hip_fail(e);
+  g_scratch[device] = ptr;
+  return ATTNRES_OK;
+}
+
 // The device a call's kernels run on: the stream's (the current device for
 // the null stream), whatever device is current.
 int launch_device(hipStream_t s, int *dev) {
@@ -1383,7 +1421,9 @@ int compute_units(int dev, int *cus) {
   return ATTNRES_OK;
 }
 
-int fwd_impl(const FwdArgs &a, void *stream, int path) {
+// noalloc: the split path takes the static scratch instead of the allocated
+// workspace, and no stream hand-off is made (calls that overlap race).
+int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
   if (path != ATTNRES_PATH_AUTO && path != ATTNRES_PATH_ROW && path != ATTNRES_PATH_SPLIT &&
       path != ATTNRES_PATH_ANY_H)
     return ATTNRES_E_PATH;
@@ -1446,13 +1486,24 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
     hipError_t e = hipStreamIsCapturing(s, &st);
     if (e != hipSuccess) return hip_fail(e);
     const bool capturing = st != hipStreamCaptureStatusNone;
+    if (noalloc) {
+      if (!g_scratch[dev]) {
+        if (capturing) return ATTNRES_E_NOT_INIT;
+        rc = static_scratch_locked(dev);
+        if (rc != ATTNRES_OK) return rc;
+      }
+      kp.ws_part = static_cast<uint64_t *>(g_scratch[dev]);
+      kp.ws_flag = reinterpret_cast<unsigned *>(static_cast<char *>(g_scratch[dev]) + kPartBytes);
+    }
     DeviceWorkspace &w = g_ws[dev];
-    if (!w.base) {
+    if (noalloc) {
+      // nothing to allocate or order
+    } else if (!w.base) {
       if (capturing) return ATTNRES_E_NOT_INIT;
       rc = init_device_locked(dev);
       if (rc != ATTNRES_OK) return rc;
     }
-    if (!capturing) {
+    if (!capturing && !noalloc) {
       if (w.has_last && w.last_stream != s) {
         e = hipEventRecord(w.handoff, w.last_stream);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, w.handoff, 0);
@@ -1461,8 +1512,10 @@ int fwd_impl(const FwdArgs &a, void *stream, int path) {
       w.last_stream = s;
       w.has_last = true;
     }
-    kp.ws_part = w.part;
-    kp.ws_flag = w.flag;
+    if (!noalloc) {
+      kp.ws_part = w.part;
+      kp.ws_flag = w.flag;
+    }
   }
 
   const bool has_d = a.delta != nullptr, has_o = a.output_norm_weight != nullptr;
@@ -1575,6 +1628,21 @@ extern "C" int attnres_fwd_strided(void *prefix, int64_t prefix_stride, const vo
                   stream, path);
 }
 
+extern "C" int attnres_fwd_noalloc(void *prefix, int64_t prefix_stride, const void *delta,
+                                   int64_t delta_stride, void *blocks,
+                                   int64_t block_token_stride, int64_t block_slot_stride,
+                                   int max_blocks, int num_blocks, const void *res_w,
+                                   const void *rms_w, float rms_eps,
+                                   const void *output_norm_weight, float output_norm_eps,
+                                   int block_write_idx, void *out, int64_t out_stride, int64_t T,
+                                   int64_t H, void *stream, int path) {
+  return fwd_impl(make_args(prefix, prefix_stride, delta, delta_stride, blocks,
+                            block_token_stride, block_slot_stride, max_blocks, num_blocks, res_w,
+                            rms_w, rms_eps, output_norm_weight, output_norm_eps, block_write_idx,
+                            out, out_stride, T, H),
+                  stream, path, /*noalloc=*/true);
+}
+
 extern "C" int attnres_init(int device) {
   if (device < 0 || device >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
   int n = 0;
@@ -1582,7 +1650,9 @@ extern "C" int attnres_init(int device) {
   if (e != hipSuccess) return hip_fail(e);
   if (device >= n) return ATTNRES_E_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  return init_device_locked(device);
+  const int rc = init_device_locked(device);
+  if (rc != ATTNRES_OK) return rc;
+  return static_scratch_locked(device);
 }
 
 extern "C" void attnres_shutdown(void) {
@@ -1604,22 +1674,28 @@ extern "C" void attnres_shutdown(void) {
 extern "C" int attnres_device_status(int device) {
   if (device < 0 || device >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  DeviceWorkspace &w = g_ws[device];
-  if (!w.base) return ATTNRES_OK;
+  // The allocated workspace and, once attnres_fwd_noalloc has used it on this
+  // device, the static scratch.
+  void *bases[2] = {g_ws[device].base, g_scratch[device]};
+  if (!bases[0] && !bases[1]) return ATTNRES_OK;
   int prev = 0;
   hipError_t e = hipGetDevice(&prev);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e);
-  unsigned flag = 0;
   e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipMemcpy(&flag, w.flag, sizeof flag, hipMemcpyDeviceToHost);
   int rc = ATTNRES_OK;
-  if (e == hipSuccess && flag != 0) {
-    // A wait gave up: parts of a token may disagree on the generation, so
-    // restart every word at generation zero.
-    e = hipMemset(w.base, 0, kWorkspaceBytes);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    rc = ATTNRES_E_DEVICE_WAIT;
+  for (void *base : bases) {
+    if (!base || e != hipSuccess) continue;
+    unsigned flag = 0;
+    e = hipMemcpy(&flag, static_cast<char *>(base) + kPartBytes, sizeof flag,
+                  hipMemcpyDeviceToHost);
+    if (e == hipSuccess && flag != 0) {
+      // A wait gave up: parts of a token may disagree on the generation, so
+      // restart every word at generation zero.
+      e = hipMemset(base, 0, kWorkspaceBytes);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+      rc = ATTNRES_E_DEVICE_WAIT;
+    }
   }
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return hip_fail(e);
