@@ -449,7 +449,8 @@ def load_ceiling_probe():
     return lib
 
 
-def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168):
+def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168,
+                  eager: bool = False):
     """The traffic of a call without its arithmetic (bench_ceiling.hip), in the
     row kernel's launch shape, over enough input sets to exceed the Infinity
     Cache: the rate this access pattern reaches on the device.  Each
@@ -478,7 +479,10 @@ def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168):
         for fn in calls:
             fn()
         torch.cuda.synchronize()
-        t = time_graph(calls, steps, replays=3, min_calls=MIN_TIMED_CALLS)
+        if eager:  # plain launches, one dispatch per call (for counter runs)
+            t = [time_eager(calls, steps)]
+        else:
+            t = time_graph(calls, steps, replays=3, min_calls=MIN_TIMED_CALLS)
         us = pct([x / steps * 1e3 for x in t], 50)
         nbytes = 2 * H * T * 13
         res[name] = dict(T=T, us=round(us, 2), GBps=round(nbytes / us / 1e3, 1),
@@ -486,7 +490,7 @@ def bench_ceiling(steps: int = 300, call_bytes: int = 190883840, H: int = 7168):
         log(f"ceiling probe {name}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
         del sets
         torch.cuda.empty_cache()
-    for name, reads, wd, wi in CEILING_CONFIGS:
+    for name, reads, wd, wi in ([] if eager else CEILING_CONFIGS):
         T = max(1, round(call_bytes / (2 * H * (reads + wd + wi))))
         footprint = 2 * H * T * (reads + wd)
         nsets = max(1, -(-2 * MALL_BYTES // footprint))
@@ -727,6 +731,86 @@ def summarize_profile(trace_dir, fetch_dir, write_dir, commands):
     print(json.dumps(out, indent=1))
 
 
+def write_counter_summary(out_name, title, commands, runs):
+    """profiles/<out_name>: the per-dispatch median of every counter of each
+    counter run (rocprofv3 --pmc, counter_collection.csv), by kernel, for the
+    libattnres kernels and the traffic probes, plus ratios derived from them.
+    `runs` maps a run label to its output directory; a label "tag/name"
+    puts "tag" before the kernel names of that run (e.g. two versions of one
+    kernel side by side)."""
+    os.makedirs(PROFILES, exist_ok=True)
+    table = {}   # kernel -> counter -> [values]
+    durations = {}
+    for label, d in runs.items():
+        for r in _csv_rows(d, "counter_collection.csv"):
+            name = _col(r, "Kernel_Name", "Kernel-Name", "KernelName")
+            m = re.search(r"((?:attnres_\w+_kernel|mid_kernel|ceiling_kernel)<[^>]*>)", name)
+            if not m:
+                continue
+            k = m.group(1)
+            if "/" in label:
+                k = label.split("/", 1)[0] + " " + k
+            ctr = _col(r, "Counter_Name", "Counter-Name", "CounterName")
+            table.setdefault(k, {}).setdefault(ctr, []).append(
+                float(_col(r, "Counter_Value", "Counter-Value", "CounterValue")))
+            try:
+                dur = (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3
+                durations.setdefault(k, {}).setdefault(
+                    int(_col(r, "Dispatch_Id", "Dispatch-Id", "DispatchId")), dur)
+            except (KeyError, ValueError):
+                pass
+    kernels = sorted(table)
+    ctrs = sorted({c for k in kernels for c in table[k]})
+    med = {k: {c: float(np.median(table[k][c])) for c in table[k]} for k in kernels}
+    lines = [f"# rocprofv3 counters, {title}", f"# kernel source hash: {kernel_source_hash()}"]
+    lines += [f"# command: {c}" for c in commands]
+    lines += ["# per-dispatch medians; counter | " + " | ".join(kernels)]
+    for c in ctrs:
+        lines.append(" | ".join([c] + [f"{med[k][c]:.6g}" if c in med[k] else "-" for k in kernels]))
+
+    def ratio(k, a, b):
+        x, y = med[k].get(a), med[k].get(b)
+        return None if x is None or not y else x / y
+
+    derived = [
+        ("wave lifetime, cycles (SQ_WAVE_CYCLES / SQ_WAVES)", "SQ_WAVE_CYCLES", "SQ_WAVES"),
+        ("waves resident per busy cycle (SQ_LEVEL_WAVES / SQ_BUSY_CYCLES)", "SQ_LEVEL_WAVES",
+         "SQ_BUSY_CYCLES"),
+        ("share of wave time waiting on memory or a barrier (SQ_WAIT_ANY / SQ_WAVE_CYCLES)",
+         "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+        ("share of wave time waiting to issue (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)",
+         "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+        ("share of wave time issuing (SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES)", "SQ_ACTIVE_INST_ANY",
+         "SQ_WAVE_CYCLES"),
+        ("VALU issue per wave-cycle (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES)", "SQ_ACTIVE_INST_VALU",
+         "SQ_WAVE_CYCLES"),
+        ("VALU instructions per wave (SQ_INSTS_VALU / SQ_WAVES)", "SQ_INSTS_VALU", "SQ_WAVES"),
+        ("vector loads per wave (SQ_INSTS_VMEM_RD / SQ_WAVES)", "SQ_INSTS_VMEM_RD", "SQ_WAVES"),
+        ("vector stores per wave (SQ_INSTS_VMEM_WR / SQ_WAVES)", "SQ_INSTS_VMEM_WR", "SQ_WAVES"),
+        ("LDS instructions per wave (SQ_INSTS_LDS / SQ_WAVES)", "SQ_INSTS_LDS", "SQ_WAVES"),
+        ("mean L2 read latency, cycles (TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum)",
+         "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum"),
+        ("mean L2 write latency, cycles (TCP_TCC_WRITE_REQ_LATENCY_sum / TCP_TCC_WRITE_REQ_sum)",
+         "TCP_TCC_WRITE_REQ_LATENCY_sum", "TCP_TCC_WRITE_REQ_sum"),
+        ("GPU busy cycles per dispatch (GRBM_GUI_ACTIVE)", "GRBM_GUI_ACTIVE", None),
+    ]
+    lines += ["#", "# derived (same dispatches' medians); quantity | " + " | ".join(kernels)]
+    for label, a, b in derived:
+        vals = [med[k].get(a) if b is None else ratio(k, a, b) for k in kernels]
+        if all(v is None for v in vals):
+            continue
+        lines.append(" | ".join([label] + ["-" if v is None else f"{v:.4g}" for v in vals]))
+    if durations:
+        lines += ["#", "# dispatch duration under counter collection, median us | " +
+                  " | ".join(kernels)]
+        lines.append(" | ".join(["duration"] + [
+            f"{float(np.median(list(durations[k].values()))):.3f}" if k in durations else "-"
+            for k in kernels]))
+    with open(os.path.join(PROFILES, out_name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -749,7 +833,16 @@ def main():
     ap.add_argument("--profile-commands", default=None, help="JSON of the commands that made them")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT_NAME", "TITLE", "COMMAND"),
                     help="write one kernel-statistics summary into profiles/")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("OUT_NAME", "TITLE"),
+                    help="write a counter summary into profiles/ from --counter-run LABEL=DIR "
+                         "directories (rocprofv3 --pmc CSV output)")
+    ap.add_argument("--counter-run", action="append", default=[], metavar="LABEL=DIR")
+    ap.add_argument("--counter-command", action="append", default=[], metavar="CMD")
     args = ap.parse_args()
+    if args.summarize_counters:
+        write_counter_summary(*args.summarize_counters, args.counter_command,
+                              dict(r.split("=", 1) for r in args.counter_run))
+        return
     if args.summarize_trace:
         write_kernel_stats(*args.summarize_trace)
         return
@@ -821,8 +914,8 @@ def main():
                                                                      args.eager)
     decode = None if (args.only in ("mid", "ceiling") or args.eager) else bench_decode(args.steps)
     longp = None if (args.only or args.eager) else bench_long()
-    ceiling = (bench_ceiling() if (args.only == "ceiling" or (args.only is None and not args.eager))
-               else None)
+    ceiling = (bench_ceiling(steps=args.steps if args.eager else 300, eager=args.eager)
+               if (args.only == "ceiling" or (args.only is None and not args.eager)) else None)
     if A.attnres_device_status() != A.ATTNRES_OK:
         raise SystemExit("device wait flag raised during the benchmark")
     cpu = None if (args.no_cpu or args.only) else cpu_baseline()

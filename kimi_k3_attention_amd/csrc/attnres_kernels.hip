@@ -219,6 +219,11 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// v of lane `src` (any lane of the wave), through the LDS crossbar.
+__device__ __forceinline__ float lane_shuffle(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
 // One token's data for SPL segments per lane: segment i of this lane is
 // seg0 + i * seg_step.  Everything is issued in one burst: the L2-resident
 // weights first (the wait counter is in order, so the query can be formed
@@ -299,19 +304,26 @@ struct Token {
     const uint16_t *prow = p.prefix + t * p.prefix_stride;
     if constexpr (CACHE_RW) {
       // The in-place rows (the written slot, a source here, and prefix when
-      // a delta rewrites it) are read through the cache; the slot is chosen
-      // at run time.
+      // a delta rewrites it) are read through the cache.  The slot is chosen
+      // at run time, so the sources are taken in a different order with no
+      // branch: the other slots ascending (streamed, a scalar index skipping
+      // widx), then slot widx; the mixture is the same sum in another order.
+      // A branch per slot would leave the compiler unable to count the loads
+      // in flight, and every source's arithmetic would wait for all of them.
       static_assert(NB > 0, "a rewritten source row needs a source slot");
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const uint16_t *row = bank + j * p.slot_stride;
-        if (j == p.widx) {
+      for (int k = 0; k + 1 < NB; ++k) {
+        const int slot = k + (k >= p.widx ? 1 : 0);
+        const uint16_t *row = bank + slot * p.slot_stride;
 #pragma unroll
-          for (int i = 0; i < SPL; ++i) x[j][i] = load_rewritten(p, row, sb[i]);
-        } else {
+        for (int i = 0; i < SPL; ++i) x[k][i] = load_row(at(row, sb[i]), ok[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        const uint16_t *row = bank + p.widx * p.slot_stride;
 #pragma unroll
-          for (int i = 0; i < SPL; ++i) x[j][i] = load_row(at(row, sb[i]), ok[i]);
-        }
+        for (int i = 0; i < SPL; ++i) x[NB - 1][i] = load_rewritten(p, row, sb[i]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (DELTA) {
 #pragma unroll
@@ -321,11 +333,16 @@ struct Token {
         for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(at(prow, sb[i]), ok[i]);
       }
     } else {
+      // Rows are issued in source order (the scheduler would otherwise order
+      // them by when their addresses are ready), so that the partials of each
+      // source can start as soon as its own rows land.
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
           x[j][i] = load_row(at(bank + j * p.slot_stride, sb[i]), ok[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(at(prow, sb[i]), ok[i]);
     }
@@ -379,23 +396,27 @@ struct Token {
     }
   }
 
-  // Per-lane partial sum of squares and query dot of every source.
+  // Per-lane partial sum of squares and query dot of source j.
+  __device__ __forceinline__ void partial(int j, const u32x4 (&qh)[SPL], const u32x4 (&ql)[SPL],
+                                          float &ss, float &dq) const {
+    float s = 0.f, dd = 0.f;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s = dot2(x[j][i][k], x[j][i][k], s);
+        dd = dot2(qh[i][k], x[j][i][k], dd);
+        dd = dot2(ql[i][k], x[j][i][k], dd);
+      }
+    ss = s;
+    dq = dd;
+  }
+
+  // The same for every source.
   __device__ __forceinline__ void partials(const u32x4 (&qh)[SPL], const u32x4 (&ql)[SPL],
                                            float (&ss)[NS], float (&dq)[NS]) const {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      float s = 0.f, dd = 0.f;
-#pragma unroll
-      for (int i = 0; i < SPL; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          s = dot2(x[j][i][k], x[j][i][k], s);
-          dd = dot2(qh[i][k], x[j][i][k], dd);
-          dd = dot2(ql[i][k], x[j][i][k], dd);
-        }
-      ss[j] = s;
-      dq[j] = dd;
-    }
+    for (int j = 0; j < NS; ++j) partial(j, qh, ql, ss[j], dq[j]);
   }
 
   // Hides the packed rows from the optimiser between the reduction and the
@@ -408,15 +429,42 @@ struct Token {
       for (int i = 0; i < SPL; ++i) asm volatile("" : "+v"(x[j][i]));
   }
 
-  // y = sum_j p_j x_j over the raw rows, fp32; p_j is read from lane j as a
-  // scalar operand.
+  // y = sum_j p_j x_j over the raw rows, fp32 accumulation; lane j holds p_j.
+  // Sources go in pairs (a, b): one byte permute gathers (x_a[h], x_b[h]) of
+  // an element pair's two elements each, and two packed bf16 dot products add
+  // p_a x_a[h] + p_b x_b[h] with each weight split into two bf16 values,
+  // p = p_hi + p_lo, p_lo = bf16(p - p_hi).  That keeps 16 significant bits
+  // of p (relative error at most 2^-17, 2^8 below the output's bf16 rounding),
+  // and every product is exact in fp32: 1.5 instructions per element and
+  // source instead of an unpack and an FMA.  An odd last source is unpacked
+  // and multiplied by the full fp32 weight.
   __device__ __forceinline__ void mix(float p_lane, float (&y)[SPL][8]) const {
 #pragma unroll
     for (int i = 0; i < SPL; ++i)
 #pragma unroll
       for (int k = 0; k < 8; ++k) y[i][k] = 0.f;
+    // lane j: (bf16(p_j), bf16(p_j - bf16(p_j))) in one word
+    const uint32_t hi = pack_bf16x2(p_lane, 0.f);
+    const uint32_t halves = pack_bf16x2(p_lane, p_lane - bf_lo(hi));
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
+    for (int a = 0; a + 1 < NS; a += 2) {
+      const uint32_t wa = uint32_t(__builtin_amdgcn_readlane(int(halves), a));
+      const uint32_t wb = uint32_t(__builtin_amdgcn_readlane(int(halves), a + 1));
+      const uint32_t ph = (wa & 0xffffu) | (wb << 16);          // (pa_hi, pb_hi)
+      const uint32_t pl = (wa >> 16) | (wb & 0xffff0000u);      // (pa_lo, pb_lo)
+#pragma unroll
+      for (int i = 0; i < SPL; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // {S0 = x_b, S1 = x_a}: bytes 0-3 are x_a's, 4-7 x_b's
+          const uint32_t lo2 = __builtin_amdgcn_perm(x[a + 1][i][k], x[a][i][k], 0x05040100u);
+          const uint32_t hi2 = __builtin_amdgcn_perm(x[a + 1][i][k], x[a][i][k], 0x07060302u);
+          y[i][2 * k] = dot2(pl, lo2, dot2(ph, lo2, y[i][2 * k]));
+          y[i][2 * k + 1] = dot2(pl, hi2, dot2(ph, hi2, y[i][2 * k + 1]));
+        }
+    }
+    if constexpr (NS % 2 == 1) {
+      constexpr int j = NS - 1;
       const float pj = lane_value(p_lane, j);
 #pragma unroll
       for (int i = 0; i < SPL; ++i)
@@ -565,6 +613,15 @@ __device__ __forceinline__ float sum_row_partials(const float *v) {
   return sum_float4s<kRowRows / 4>(reinterpret_cast<const float4 *>(v));
 }
 
+// Sum of n (<= 64) row partials, one per lane, over the wave in a fixed order
+// (DPP), returned in every lane: one LDS read per lane instead of a lane
+// summing all n.
+__device__ __forceinline__ float wave_sum_of_partials(const float *v, int n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float x = lane < n ? v[lane] : 0.f;
+  return lane_value(wave_sum_lane63(x), kWave - 1);
+}
+
 // The grid either has one workgroup per token or is persistent (a few
 // workgroups per CU looping over tokens); LDS partials are double-buffered by
 // iteration parity so one barrier per phase suffices.
@@ -610,40 +667,44 @@ attnres_row_kernel(KParams p) {
         const float sy = row16_sum(sum_sq<SPL>(y));
         if (row_leader) s_ysq[par][rowslot] = sy;
         __syncthreads();
-        rsig = rsqrtf(sum_row_partials(s_ysq[par]) * kInvHidden + p.out_eps);
+        rsig = rsqrtf(wave_sum_of_partials(s_ysq[par], kRowRows) * kInvHidden + p.out_eps);
       }
       tk.store(p, t, seg0, seg_step, y, rsig);
       continue;
     }
     u32x4 qh[SPL], ql[SPL];
     tk.query(qh, ql);
-    tk.finish_cur();
-    if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, seg0, seg_step);
 
-    float ss[NS], dq[NS];
-    tk.partials(qh, ql, ss, dq);
-    tk.keep_packed();
+    // Each source's partials as soon as its rows land (loads retire in issue
+    // order: the bank rows, then prefix and delta), reduced within 16-lane
+    // rows and parked in LDS, so that this work overlaps the later rows'
+    // arrival; cur (prefix + delta, issued last) comes last.
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      ss[j] = row16_sum(ss[j]);
-      dq[j] = row16_sum(dq[j]);
-    }
-    if (row_leader) {
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        s_part[par][j][rowslot] = ss[j];
-        s_part[par][NS + j][rowslot] = dq[j];
+      if (j == NB) {
+        tk.finish_cur();
+        if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, seg0, seg_step);
       }
+      float sj, dj;
+      tk.partial(j, qh, ql, sj, dj);
+      sj = row16_sum(sj);
+      dj = row16_sum(dj);
+      if (row_leader) {
+        s_part[par][j][rowslot] = sj;
+        s_part[par][NS + j][rowslot] = dj;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    tk.keep_packed();
     __syncthreads();
     tk.issue_onw(p, seg0, seg_step);
 
-    float logit = 0.f;
-    if (lane < NS) {
-      const float s = sum_row_partials(s_part[par][lane]);
-      const float d = sum_row_partials(s_part[par][NS + lane]);
-      logit = d * rsqrtf(s * kInvHidden + p.rms_eps);
-    }
+    // Lane j < NS sums source j's squares and lane 32 + j its query dots;
+    // lane j then takes the dot from lane 32 + j.
+    float tot = 0.f;
+    if ((lane & 31) < NS) tot = sum_row_partials(s_part[par][(lane & 31) + (lane >> 5) * NS]);
+    const float dq_j = lane_shuffle(tot, (lane + 32) & (kWave - 1));
+    const float logit = lane < NS ? dq_j * rsqrtf(tot * kInvHidden + p.rms_eps) : 0.f;
     const float p_lane = softmax_lanes<NS>(logit);
     float y[SPL][8];
     tk.keep_packed();
@@ -654,7 +715,7 @@ attnres_row_kernel(KParams p) {
       const float sy = row16_sum(sum_sq<SPL>(y));
       if (row_leader) s_ysq[par][rowslot] = sy;
       __syncthreads();
-      rsig = rsqrtf(sum_row_partials(s_ysq[par]) * kInvHidden + p.out_eps);
+      rsig = rsqrtf(wave_sum_of_partials(s_ysq[par], kRowRows) * kInvHidden + p.out_eps);
     }
     tk.store(p, t, seg0, seg_step, y, rsig);
   }
@@ -726,39 +787,37 @@ attnres_anyh_kernel(KParams p) {
       const float sy = row16_sum(sum_sq<SPL>(y));
       if (row_leader) s_ysq[rowslot] = sy;
       __syncthreads();
-      rsig = rsqrtf(sum_row_partials_n(s_ysq, n4) * p.inv_h + p.out_eps);
+      rsig = rsqrtf(wave_sum_of_partials(s_ysq, 4 * n4) * p.inv_h + p.out_eps);
     }
     tk.store(p, t, seg0, seg_step, y, rsig);
     return;
   }
   u32x4 qh[SPL], ql[SPL];
   tk.query(qh, ql);
-  tk.finish_cur();
 
-  float ss[NS], dq[NS];
-  tk.partials(qh, ql, ss, dq);
-  tk.keep_packed();
+  // Each source's partials as its rows land, cur last (as in the row kernel).
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    ss[j] = row16_sum(ss[j]);
-    dq[j] = row16_sum(dq[j]);
-  }
-  if (row_leader) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      s_part[j][rowslot] = ss[j];
-      s_part[NS + j][rowslot] = dq[j];
+    if (j == NB) tk.finish_cur();
+    float sj, dj;
+    tk.partial(j, qh, ql, sj, dj);
+    sj = row16_sum(sj);
+    dj = row16_sum(dj);
+    if (row_leader) {
+      s_part[j][rowslot] = sj;
+      s_part[NS + j][rowslot] = dj;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  tk.keep_packed();
   __syncthreads();
   tk.issue_onw(p, seg0, seg_step);
 
-  float logit = 0.f;
-  if (lane < NS) {
-    const float s = sum_row_partials_n(s_part[lane], n4);
-    const float d = sum_row_partials_n(s_part[NS + lane], n4);
-    logit = d * rsqrtf(s * p.inv_h + p.rms_eps);
-  }
+  // Lane j < NS sums source j's squares, lane 32 + j its query dots.
+  float tot = 0.f;
+  if ((lane & 31) < NS) tot = sum_row_partials_n(s_part[(lane & 31) + (lane >> 5) * NS], n4);
+  const float dq_j = lane_shuffle(tot, (lane + 32) & (kWave - 1));
+  const float logit = lane < NS ? dq_j * rsqrtf(tot * p.inv_h + p.rms_eps) : 0.f;
   const float p_lane = softmax_lanes<NS>(logit);
   float y[SPL][8];
   tk.keep_packed();
@@ -769,7 +828,7 @@ attnres_anyh_kernel(KParams p) {
     const float sy = row16_sum(sum_sq<SPL>(y));
     if (row_leader) s_ysq[rowslot] = sy;
     __syncthreads();
-    rsig = rsqrtf(sum_row_partials_n(s_ysq, n4) * p.inv_h + p.out_eps);
+    rsig = rsqrtf(wave_sum_of_partials(s_ysq, 4 * n4) * p.inv_h + p.out_eps);
   }
   tk.store(p, t, seg0, seg_step, y, rsig);
 }
@@ -842,10 +901,6 @@ __device__ __forceinline__ float gather(const uint64_t *tok_ws, int idx, uint32_
     s1 += value_of(w[r + 1]);
   }
   return s0 + s1;
-}
-
-__device__ __forceinline__ float lane_shuffle(float v, int src) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
 // Row j of the upper-triangular pair list (j <= k, row-major) starts here.

@@ -135,3 +135,24 @@ def test_kernel_trace_average_read_only_for_current_source(profiles_dir, monkeyp
     body[2] = "# kernel source hash: other"
     f.write_text("\n".join(body) + "\n")
     assert bench.load_kernel_trace_us() is None
+
+
+def test_counter_summary_medians_and_ratios(tmp_path, profiles_dir):
+    """Per-dispatch medians by kernel, and the derived ratios from them."""
+    ours = f"void attnres::(anonymous namespace)::{bench.DOMINANT_KERNEL}(attnres::KParams)"
+    probe = "void (anonymous namespace)::mid_kernel<true>(u32x4*, u32x4*, u32x4 const*, u32x4*, long)"
+    rows = []
+    for k, (w, c) in enumerate([(100.0, 5000.0), (100.0, 7000.0), (100.0, 6000.0)]):
+        rows += [[k, ours, "SQ_WAVES", w, 0, 1000], [k, ours, "SQ_WAVE_CYCLES", c, 0, 1000]]
+    rows += [[9, probe, "SQ_WAVES", 50.0, 0, 2000], [9, probe, "SQ_WAVE_CYCLES", 1000.0, 0, 2000]]
+    _write_csv(str(tmp_path / "run" / "a_counter_collection.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                "End_Timestamp"], rows)
+    bench.write_counter_summary("c.txt", "t", ["cmd1"], {"k": str(tmp_path / "run")})
+    text = (profiles_dir / "c.txt").read_text()
+    assert "# command: cmd1" in text
+    kernels = ["attnres_row_kernel<8, true, true, true>", "mid_kernel<true>"]
+    assert text.count(" | ".join(["# per-dispatch medians; counter"] + kernels)) == 1
+    assert "SQ_WAVE_CYCLES | 6000 | 1000" in text
+    assert "wave lifetime, cycles (SQ_WAVE_CYCLES / SQ_WAVES) | 60 | 20" in text
+    assert "duration | 1.000 | 2.000" in text
