@@ -113,7 +113,8 @@ class Set:
                           c.widx, self.out[sl], path=path)
 
 
-def time_graph(calls, steps: int, replays: int = 1, warm: int = 1, min_calls: int = 0):
+def time_graph(calls, steps: int, replays: int = 1, warm: int = 1, min_calls: int = 0,
+               stream=None):
     """Captures `steps` calls (cycling over `calls`) into one hipGraph and
     returns, for each of `replays` timed samples, the elapsed ms per graph
     replay, after `warm` untimed replays (graph upload, first touch of the
@@ -121,10 +122,11 @@ def time_graph(calls, steps: int, replays: int = 1, warm: int = 1, min_calls: in
     back to back between one pair of hipEvents on the launch stream, with no
     host synchronisation inside, so the graph's fixed start-up cost is spread
     over at least `min_calls` calls whatever `steps` is; the sample's time is
-    divided by R."""
+    divided by R.  `stream`: the stream to capture on (torch's own by
+    default)."""
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=stream):
         for i in range(steps):
             calls[i % len(calls)]()
     torch.cuda.synchronize()
@@ -285,6 +287,86 @@ def bench_long(steps: int = 20):
         log(f"long prefill T={T}: {us:.1f} us, {res[f'T{T}']['GBps']:.0f} GB/s")
         del s
         torch.cuda.empty_cache()
+    return res
+
+
+OVERLAP_TOKENS = (1, 4, 16, 64)
+
+
+def bench_overlap(n: int = 4096, steps: int = 1200):
+    """The two-kernel form beside a producer of delta, against the one-kernel
+    call after it.  A step is the producer (delta = x W, a [T, 7168] x
+    [7168, 7168] bf16 product, the shape of a projection that produces the
+    residual update) followed by the attention-residual call of the same T
+    tokens (8 or 4 block rows, delta and output norm).  Three graphs of `steps`
+    steps are timed: the producer alone; producer -> attnres_fwd; and, per
+    step, a fork: attnres_fwd_bank on a side branch while the producer runs,
+    joined before attnres_fwd_cur.  The exposed attention-residual time is a
+    graph's time per step minus the producer's.  Consecutive steps take
+    consecutive T-token windows of one resident input (decode recipe)."""
+    case = W.Case("overlap", T=n, nb=8, recipe="decode", seed=1)
+    st = Set(W.make_inputs(case))
+    H = case.H
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    x = (0.01 * torch.randn(n, H, device="cuda", generator=gen)).to(torch.bfloat16)
+    wmat = (torch.randn(H, H, device="cuda", generator=gen) / H ** 0.5).to(torch.bfloat16)
+    delta = st.delta.view(torch.bfloat16)
+    # The matrix product's library sets itself up on first use on a stream,
+    # which graph capture does not allow: run it once on the capture stream.
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for T in OVERLAP_TOKENS:
+            torch.mm(x[:T], wmat, out=delta[:T])
+    torch.cuda.synchronize()
+    res = {}
+    for T in OVERLAP_TOKENS:
+        windows = n // T
+        nbytes = A.attnres_partial_bytes(T, H)
+        # one partial-state buffer per window, each 256-byte aligned
+        parts = torch.empty(windows, -(-nbytes // 256) * 64, dtype=torch.float32, device="cuda")
+        side = torch.cuda.Stream()
+        for nb in (8, 4):
+            def args(w, nb=nb):
+                sl = slice(w * T, (w + 1) * T)
+                return (st.prefix[sl], st.delta[sl], st.bank3[sl], nb, st.res_w, st.rms_w,
+                        case.eps, st.onw, case.oeps, -1, st.out[sl])
+
+            def produce(w):
+                sl = slice(w * T, (w + 1) * T)
+                torch.mm(x[sl], wmat, out=delta[sl])
+
+            def chain(w):
+                produce(w)
+                A.attnres_fwd(*args(w))
+
+            def fork(w):
+                main = torch.cuda.current_stream()
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    A.attnres_fwd_bank(*args(w), parts[w], stream=side)
+                produce(w)
+                main.wait_stream(side)
+                A.attnres_fwd_cur(*args(w), parts[w], stream=main)
+
+            cell = {}
+            for name, fn in (("producer", produce), ("chain", chain), ("two_kernel", fork)):
+                calls = [lambda w=w, fn=fn: fn(w) for w in range(windows)]
+                with torch.cuda.stream(cap):
+                    for c in calls[:4]:
+                        c()
+                torch.cuda.synchronize()
+                t = time_graph(calls, min(steps, max(windows, 300)), replays=3, warm=2,
+                               stream=cap)
+                k = min(steps, max(windows, 300))
+                cell[name] = round(pct([v / k * 1e3 for v in t], 50), 3)
+            cell["exposed_chain"] = round(cell["chain"] - cell["producer"], 3)
+            cell["exposed_two_kernel"] = round(cell["two_kernel"] - cell["producer"], 3)
+            cell["saved_per_step"] = round(cell["chain"] - cell["two_kernel"], 3)
+            res[f"T{T}_nb{nb}"] = cell
+            log(f"overlap T={T} nb={nb}: " + ", ".join(f"{k} {v}" for k, v in cell.items()))
+        del parts
+    res["extra_bytes_per_token"] = 2 * 4 * H + 8  # u written and read back, (m, s)
     return res
 
 
@@ -826,6 +908,9 @@ def main():
                     help="small batches: row vs split kernel over T and num_blocks")
     ap.add_argument("--variant-sweep", action="store_true",
                     help="only T=1024 calls over num_blocks x delta x output norm")
+    ap.add_argument("--overlap", action="store_true",
+                    help="only the two-kernel form beside a producer of delta, against the "
+                         "one-kernel call after it")
     ap.add_argument("--configs", action="store_true",
                     help="only the reference case (T=4, nb=4) and the 80-case variant matrix")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -867,6 +952,19 @@ def main():
     A.attnres_init()
     if args.calibrate:
         calibration_copy()
+    if args.overlap:
+        table = bench_overlap()
+        print(json.dumps({"metric": "exposed attention-residual time per decode step beside "
+                                    "the producer of delta", "unit": "us/step",
+                          "higher_is_better": False, "data": "synthetic",
+                          "config": {"workload": "T tokens (1/4/16/64), H=7168, 8 or 4 block "
+                                                 "rows, delta and output norm, no bank write; "
+                                                 "producer delta = x W, [T,7168]x[7168,7168] "
+                                                 "bf16",
+                                     "timing": "hipGraph replay"},
+                          "steps": table, "kernel_source_hash": kernel_source_hash()}),
+              flush=True)
+        return
     if args.configs:
         table = bench_configs()
         print(json.dumps({"metric": "attention-residual forward latency and throughput per case",

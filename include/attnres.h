@@ -199,6 +199,58 @@ int attnres_fwd_noalloc(void *prefix, int64_t prefix_stride,
                         int block_write_idx, void *out, int64_t out_stride,
                         int64_t T, int64_t H, void *stream, int path);
 
+/*
+ * Two-kernel form of attnres_fwd_strided, so that the part of the work that
+ * does not depend on delta can run before delta exists.  The prhub digest of
+ * vLLM PR #54261 ("Implementation breakdown" and the kernel under "Key source
+ * snippets") describes the reference kernel's programmatic dependent launch:
+ * it issues its bank-row copies before waiting on delta's producer, and waits
+ * only before the first copy that needs the producer's output (the prefix/delta
+ * row).  HIP has no dependent launch, so the work is split in two kernels that
+ * a hipGraph (or two streams) can place beside the producer:
+ *
+ *   attnres_fwd_bank  reads only the bank rows 0..num_blocks-1 and the scoring
+ *                     weights: their logits, the online softmax state (m, s) of
+ *                     those logits, and the unnormalised mixture
+ *                     u = sum_j exp(l_j - m) x_j (fp32), into `partial`;
+ *   attnres_fwd_cur   forms cur = prefix (+ delta), its logit, merges it into
+ *                     (m, s) as one more online-softmax step, applies the
+ *                     output norm and does every store of attnres_fwd.
+ *
+ * Results equal attnres_fwd's within the fp32 rounding of a different order.
+ * Both take attnres_fwd_strided's arguments (pass the same values to both; each
+ * call validates them as attnres_fwd_strided would), plus `partial`: device
+ * memory of at least attnres_partial_bytes(T, H) bytes, 16-byte aligned, owned
+ * by the caller and not overlapping any argument (ATTNRES_E_NULL,
+ * ATTNRES_E_ALIGN, ATTNRES_E_SHAPE for too small, ATTNRES_E_ALIAS).  It may be
+ * NULL when num_blocks == 0 (attnres_fwd_bank then launches nothing).  The
+ * caller orders attnres_fwd_cur after attnres_fwd_bank of the same call, and
+ * the next call's attnres_fwd_bank after this call's attnres_fwd_cur when the
+ * two share `partial` or bank rows.  attnres_fwd_bank writes only `partial`.
+ * Layout of `partial`: u as fp32 [T, H], then (m, s) as two fp32 per token.
+ * Neither kernel allocates memory or uses the split path's workspace, so both
+ * can be captured into a hipGraph.
+ */
+int64_t attnres_partial_bytes(int64_t T, int64_t H);  /* < 0: an error code */
+int attnres_fwd_bank(const void *prefix, int64_t prefix_stride,
+                     const void *delta, int64_t delta_stride, const void *blocks,
+                     int64_t block_token_stride, int64_t block_slot_stride,
+                     int max_blocks, int num_blocks,
+                     const void *res_w, const void *rms_w, float rms_eps,
+                     const void *output_norm_weight, float output_norm_eps,
+                     int block_write_idx, const void *out, int64_t out_stride,
+                     int64_t T, int64_t H, void *partial, int64_t partial_bytes,
+                     void *stream);
+int attnres_fwd_cur(void *prefix, int64_t prefix_stride,
+                    const void *delta, int64_t delta_stride, void *blocks,
+                    int64_t block_token_stride, int64_t block_slot_stride,
+                    int max_blocks, int num_blocks,
+                    const void *res_w, const void *rms_w, float rms_eps,
+                    const void *output_norm_weight, float output_norm_eps,
+                    int block_write_idx, void *out, int64_t out_stride,
+                    int64_t T, int64_t H, const void *partial, int64_t partial_bytes,
+                    void *stream);
+
 /* The host-side argument checks of attnres_fwd, alone.  Makes no HIP call and
  * dereferences no pointer, so it runs without a GPU. */
 int attnres_validate(const void *prefix, const void *delta, const void *blocks,

@@ -62,6 +62,12 @@ _lib.attnres_fwd_strided.argtypes = _STRIDED_ARGS + [_vp, _int]
 _lib.attnres_fwd_strided.restype = _int
 _lib.attnres_fwd_noalloc.argtypes = _STRIDED_ARGS + [_vp, _int]
 _lib.attnres_fwd_noalloc.restype = _int
+_lib.attnres_partial_bytes.argtypes = [_i64, _i64]
+_lib.attnres_partial_bytes.restype = _i64
+_lib.attnres_fwd_bank.argtypes = _STRIDED_ARGS + [_vp, _i64, _vp]
+_lib.attnres_fwd_bank.restype = _int
+_lib.attnres_fwd_cur.argtypes = _STRIDED_ARGS + [_vp, _i64, _vp]
+_lib.attnres_fwd_cur.restype = _int
 _lib.attnres_validate_strided.argtypes = list(_STRIDED_ARGS)
 _lib.attnres_validate_strided.restype = _int
 _lib.attnres_init.argtypes = [_int]
@@ -230,6 +236,58 @@ def attnres_fwd_noalloc(prefix: torch.Tensor, delta: Optional[torch.Tensor],
                                       ATTNRES_PATH_AUTO if path is None else int(path))
     if rc != ATTNRES_OK:
         raise AttnResError(rc, "attnres_fwd_noalloc")
+
+
+def attnres_partial_bytes(T: int, H: int) -> int:
+    """Bytes of the partial-state buffer of the two-kernel form."""
+    n = _lib.attnres_partial_bytes(int(T), int(H))
+    if n < 0:
+        raise AttnResError(int(n), "attnres_partial_bytes")
+    return n
+
+
+def _two_part(fn_name, prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps,
+              output_norm_weight, output_norm_eps, block_write_idx, out, partial, stream):
+    m = _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
+                 output_norm_eps, block_write_idx, out)
+    dev = prefix.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for name, t in (("delta", delta), ("blocks", blocks), ("res_w", res_w), ("rms_w", rms_w),
+                    ("output_norm_weight", output_norm_weight), ("out", out),
+                    ("partial", partial)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, prefix on {dev}: all tensors must be "
+                             "on the same GPU")
+    nbytes = 0 if partial is None else partial.numel() * partial.element_size()
+    if partial is not None and not partial.is_contiguous():
+        raise ValueError("partial must be contiguous")
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = getattr(_lib, fn_name)(*_strided_args(m), _ptr(partial), nbytes, s.cuda_stream)
+    if rc != ATTNRES_OK:
+        raise AttnResError(rc, fn_name)
+
+
+def attnres_fwd_bank(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps,
+                     output_norm_weight, output_norm_eps, block_write_idx, out,
+                     partial: Optional[torch.Tensor],
+                     stream: Optional[torch.cuda.Stream] = None) -> None:
+    """First kernel of the two-kernel form (the bank rows only; see
+    include/attnres.h): writes the partial state into `partial`, a contiguous
+    device tensor of at least attnres_partial_bytes(T, H) bytes."""
+    _two_part("attnres_fwd_bank", prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps,
+              output_norm_weight, output_norm_eps, block_write_idx, out, partial, stream)
+
+
+def attnres_fwd_cur(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps,
+                    output_norm_weight, output_norm_eps, block_write_idx, out,
+                    partial: Optional[torch.Tensor],
+                    stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Second kernel of the two-kernel form: cur, the merge with the bank
+    part's state, the output norm and every store of attnres_fwd."""
+    _two_part("attnres_fwd_cur", prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps,
+              output_norm_weight, output_norm_eps, block_write_idx, out, partial, stream)
 
 
 def attnres_fwd_path(*args, path: int, **kw) -> None:

@@ -41,6 +41,12 @@ struct FwdArgs {
 };
 
 int validate(const FwdArgs &a);
+// The two-kernel form's partial-state buffer: bytes it needs for T tokens of
+// hidden size H (an error code for sizes attnres_fwd rejects), and the checks
+// of a given buffer against a validated call (NULL allowed when no bank row
+// is read: num_blocks == 0 or T == 0).
+int64_t partial_bytes(int64_t T, int64_t H);
+int validate_partial(const FwdArgs &a, const void *partial, int64_t bytes);
 // The row stride actually used for a [T, H] matrix argument.
 inline int64_t row_stride(int64_t given, int64_t T, int64_t H) { return T <= 1 ? H : given; }
 const char *strerror_text(int status);

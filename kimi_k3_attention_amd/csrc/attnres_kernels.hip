@@ -145,6 +145,7 @@ struct KParams {
   float inv_h;            // 1 / H
   uint64_t *ws_part;       // split path: tagged words, 14 parts per token
   unsigned *ws_flag;
+  float *partial;          // two-kernel form: the bank part's state (see attnres_bank_kernel)
 };
 
 // ---------------------------------------------------------------------------
@@ -234,11 +235,16 @@ __device__ __forceinline__ float lane_shuffle(float v, int src) {
 // MASKED (rows whose length is not a multiple of the workgroup's reach):
 // a segment at or past p.nseg loads nothing and holds zeros, which add
 // nothing to any sum, and is never stored.
-template <int NB, bool DELTA, bool ONORM, int SPL, bool MASKED = false, bool CACHE_RW = false>
+// CUR = false: the bank rows only (the first kernel of the two-kernel form),
+// no prefix, delta or cur.  Q: load the scoring weights for the fused query
+// (needed whenever a logit is formed: with bank rows, or in the second
+// kernel of the two-kernel form, which scores cur alone).
+template <int NB, bool DELTA, bool ONORM, int SPL, bool MASKED = false, bool CACHE_RW = false,
+          bool CUR = true, bool Q = (NB > 0)>
 struct Token {
-  static constexpr int NS = NB + 1;
+  static constexpr int NS = NB + (CUR ? 1 : 0);
   u32x4 rms[SPL], res[SPL], onw[SPL];  // weights
-  u32x4 x[NS][SPL];                    // bank slots 0..NB-1, then prefix (cur after finish_cur)
+  u32x4 x[NB + 1][SPL];                // bank slots 0..NB-1, then prefix (cur after finish_cur)
   u32x4 d[SPL];                        // delta
 
   __device__ __forceinline__ static bool in_row(const KParams &p, int seg) {
@@ -294,7 +300,7 @@ struct Token {
       ok[i] = in_row(p, seg0 + i * seg_step);
       sb[i] = seg_bytes(seg0, seg_step, i);
     }
-    if constexpr (NB > 0)  // a single source needs no logit, hence no query
+    if constexpr (Q)  // a single source needs no logit, hence no query
 #pragma unroll
       for (int i = 0; i < SPL; ++i) {
         rms[i] = load_weight(at(p.rms_w, sb[i]), ok[i]);
@@ -302,7 +308,18 @@ struct Token {
       }
     const uint16_t *bank = p.blocks + t * p.tok_stride;
     const uint16_t *prow = p.prefix + t * p.prefix_stride;
-    if constexpr (CACHE_RW) {
+    if constexpr (!CUR) {
+      // The bank rows alone, in source order.
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+          x[j][i] = load_row(at(bank + j * p.slot_stride, sb[i]), ok[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    } else if constexpr (CACHE_RW) {
       // The in-place rows (the written slot, a source here, and prefix when
       // a delta rewrites it) are read through the cache.  The slot is chosen
       // at run time, so the sources are taken in a different order with no
@@ -386,7 +403,7 @@ struct Token {
   // values is within 2^-24 (relative) of the exact sum, which is never close
   // enough to a bf16 rounding boundary to change the rounded result.
   __device__ __forceinline__ void finish_cur() {
-    if constexpr (DELTA) {
+    if constexpr (CUR && DELTA) {
 #pragma unroll
       for (int i = 0; i < SPL; ++i)
 #pragma unroll
@@ -554,6 +571,29 @@ __device__ __forceinline__ float sum_sq(const float (&y)[SPL][8]) {
 // (m, s).  Then p_j = exp(l_j - m) / s, with s >= 1 (the maximum's own term
 // is 1), so the hardware reciprocal serves.  A NaN logit makes s, hence
 // every p_j, NaN.
+// The online normaliser's state (m, s) of NS logits (lane j holds logit j),
+// merged as a fixed-order tree; wave-uniform.
+template <int NS>
+__device__ __forceinline__ void softmax_state(float logit_lane, float &m_out, float &s_out) {
+  float m[NS], s[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    m[j] = lane_value(logit_lane, j);
+    s[j] = 1.f;
+  }
+#pragma unroll
+  for (int w = 1; w < NS; w *= 2)
+#pragma unroll
+    for (int j = 0; j + w < NS; j += 2 * w) {
+      const float d = m[j + w] - m[j];
+      const float e = __expf(-fabsf(d));
+      s[j] = d <= 0.f ? fmaf(s[j + w], e, s[j]) : fmaf(s[j], e, s[j + w]);
+      m[j] = fmaxf(m[j], m[j + w]);
+    }
+  m_out = m[0];
+  s_out = s[0];
+}
+
 template <int NS>
 __device__ __forceinline__ float softmax_lanes(float logit_lane) {
   if constexpr (NS == 1) {
@@ -562,22 +602,9 @@ __device__ __forceinline__ float softmax_lanes(float logit_lane) {
     return (logit_lane - logit_lane) + 1.f;
   } else {
     const int lane = threadIdx.x & (kWave - 1);
-    float m[NS], s[NS];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      m[j] = lane_value(logit_lane, j);
-      s[j] = 1.f;
-    }
-#pragma unroll
-    for (int w = 1; w < NS; w *= 2)
-#pragma unroll
-      for (int j = 0; j + w < NS; j += 2 * w) {
-        const float d = m[j + w] - m[j];
-        const float e = __expf(-fabsf(d));
-        s[j] = d <= 0.f ? fmaf(s[j + w], e, s[j]) : fmaf(s[j], e, s[j + w]);
-        m[j] = fmaxf(m[j], m[j + w]);
-      }
-    return lane < NS ? __expf(logit_lane - m[0]) * __builtin_amdgcn_rcpf(s[0]) : 0.f;
+    float m, s;
+    softmax_state<NS>(logit_lane, m, s);
+    return lane < NS ? __expf(logit_lane - m) * __builtin_amdgcn_rcpf(s) : 0.f;
   }
 }
 
@@ -823,6 +850,170 @@ attnres_anyh_kernel(KParams p) {
   tk.keep_packed();
   tk.mix(p_lane, y);
 
+  float rsig = 1.f;
+  if constexpr (ONORM) {
+    const float sy = row16_sum(sum_sq<SPL>(y));
+    if (row_leader) s_ysq[rowslot] = sy;
+    __syncthreads();
+    rsig = rsqrtf(wave_sum_of_partials(s_ysq, 4 * n4) * p.inv_h + p.out_eps);
+  }
+  tk.store(p, t, seg0, seg_step, y, rsig);
+}
+
+// ---------------------------------------------------------------------------
+// two-kernel form: the bank part (independent of delta), then the cur part
+// ---------------------------------------------------------------------------
+//
+// The bank part of token t leaves in p.partial: u_t = sum_{j < nb} exp(l_j -
+// m_t) x_j, fp32, H elements at p.partial + t H; then, after all T rows, the
+// online normaliser's state (m_t, s_t) of the bank logits l_j (two floats at
+// p.partial + T H + 2 t).  The cur part merges cur's logit l_c into that
+// state, as one more step of the online softmax: M = max(m_t, l_c),
+// S = s_t exp(m_t - M) + exp(l_c - M), y = (u_t exp(m_t - M) + cur
+// exp(l_c - M)) / S; then the output norm and every store.  Both run in the
+// any-H kernel's launch shape, one workgroup per token.
+
+template <int SPL, bool MASKED, int NB>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kWave, kAnyMaxThreads),
+                               amdgpu_waves_per_eu(SPL <= 2 ? 4 : 2)))
+attnres_bank_kernel(KParams p) {
+  static_assert(NB > 0, "the bank part needs bank rows");
+  __shared__ __align__(16) float s_part[2 * NB][kAnyMaxRows];
+
+  const int nthreads = blockDim.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int rowslot = wave * 4 + (lane >> 4);
+  const bool row_leader = (lane & 15) == 0;
+  const int n4 = nthreads / kWave;
+  const int64_t t = blockIdx.x;
+  const int seg0 = int(threadIdx.x);
+  const int seg_step = nthreads;
+
+  Token<NB, false, false, SPL, MASKED, false, /*CUR=*/false> tk;
+  tk.issue(p, t, seg0, seg_step);
+  u32x4 qh[SPL], ql[SPL];
+  tk.query(qh, ql);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    float sj, dj;
+    tk.partial(j, qh, ql, sj, dj);
+    sj = row16_sum(sj);
+    dj = row16_sum(dj);
+    if (row_leader) {
+      s_part[j][rowslot] = sj;
+      s_part[NB + j][rowslot] = dj;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  tk.keep_packed();
+  __syncthreads();
+
+  float tot = 0.f;
+  if ((lane & 31) < NB) tot = sum_row_partials_n(s_part[(lane & 31) + (lane >> 5) * NB], n4);
+  const float dq_j = lane_shuffle(tot, (lane + 32) & (kWave - 1));
+  const float logit = lane < NB ? dq_j * rsqrtf(tot * p.inv_h + p.rms_eps) : 0.f;
+  float m, sum;
+  softmax_state<NB>(logit, m, sum);
+  const float w_lane = lane < NB ? __expf(logit - m) : 0.f;
+  float u[SPL][8];
+  tk.keep_packed();
+  tk.mix(w_lane, u);
+
+  const int64_t H = int64_t(p.nseg) * kSeg;
+  float *urow = p.partial + t * H;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int seg = seg0 + i * seg_step;
+    if (MASKED && seg >= p.nseg) continue;
+    f32x4 *dst = reinterpret_cast<f32x4 *>(urow + int64_t(seg) * kSeg);
+    dst[0] = f32x4{u[i][0], u[i][1], u[i][2], u[i][3]};
+    dst[1] = f32x4{u[i][4], u[i][5], u[i][6], u[i][7]};
+  }
+  if (threadIdx.x == 0) {
+    float *st = p.partial + int64_t(p.T) * H + 2 * t;
+    st[0] = m;
+    st[1] = sum;
+  }
+}
+
+template <int SPL, bool MASKED, bool DELTA, bool ONORM, bool BANK>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kWave, kAnyMaxThreads),
+                               amdgpu_waves_per_eu(SPL <= 2 ? 4 : 2)))
+attnres_cur_kernel(KParams p) {
+  __shared__ __align__(16) float s_part[2][kAnyMaxRows];
+  __shared__ __align__(16) float s_ysq[kAnyMaxRows];
+
+  const int nthreads = blockDim.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int rowslot = wave * 4 + (lane >> 4);
+  const bool row_leader = (lane & 15) == 0;
+  const int n4 = nthreads / kWave;
+  const int64_t t = blockIdx.x;
+  const int seg0 = int(threadIdx.x);
+  const int seg_step = nthreads;
+  const int64_t H = int64_t(p.nseg) * kSeg;
+
+  // cur is the only row this part reads from the bank side; the bank's
+  // contribution arrives as the partial state.
+  Token<0, DELTA, ONORM, SPL, MASKED, false, true, /*Q=*/BANK> tk;
+  tk.issue(p, t, seg0, seg_step);
+  f32x4 u[SPL][2];
+  float m_b = 0.f, s_b = 0.f;
+  if constexpr (BANK) {
+    const float *urow = p.partial + t * H;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int seg = seg0 + i * seg_step;
+      const bool ok = !MASKED || seg < p.nseg;
+      const f32x4 *src = reinterpret_cast<const f32x4 *>(urow + int64_t(seg) * kSeg);
+      u[i][0] = ok ? src[0] : zero;
+      u[i][1] = ok ? src[1] : zero;
+    }
+    const float *st = p.partial + int64_t(p.T) * H + 2 * t;
+    m_b = st[0];
+    s_b = st[1];
+  }
+  float y[SPL][8];
+  if constexpr (BANK) {
+    u32x4 qh[SPL], ql[SPL];
+    tk.query(qh, ql);
+    tk.finish_cur();
+    float sc, dc;
+    tk.partial(0, qh, ql, sc, dc);
+    sc = row16_sum(sc);
+    dc = row16_sum(dc);
+    if (row_leader) {
+      s_part[0][rowslot] = sc;
+      s_part[1][rowslot] = dc;
+    }
+    __syncthreads();
+    tk.issue_onw(p, seg0, seg_step);
+    float tot = 0.f;
+    if ((lane & 31) == 0) tot = sum_row_partials_n(s_part[lane >> 5], n4);
+    const float lc = lane_value(tot, 32) * rsqrtf(lane_value(tot, 0) * p.inv_h + p.rms_eps);
+    // One more step of the online softmax: (m_b, s_b) merged with (lc, 1).
+    // One of the two factors is exp(0) = 1, so the normaliser is >= 1.
+    const float mx = fmaxf(m_b, lc);
+    const float fa = __expf(m_b - mx), fc = __expf(lc - mx);
+    const float inv = __builtin_amdgcn_rcpf(fmaf(s_b, fa, fc));
+    const float ca = fa * inv, cc = fc * inv;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float u0 = u[i][k >> 1][(k & 1) * 2], u1 = u[i][k >> 1][(k & 1) * 2 + 1];
+        y[i][2 * k] = fmaf(ca, u0, cc * bf_lo(tk.x[0][i][k]));
+        y[i][2 * k + 1] = fmaf(ca, u1, cc * bf_hi(tk.x[0][i][k]));
+      }
+  } else {
+    // No bank rows: cur alone, weight exactly 1.
+    tk.finish_cur();
+    tk.issue_onw(p, seg0, seg_step);
+    tk.cur_as_mix(y);
+  }
   float rsig = 1.f;
   if constexpr (ONORM) {
     const float sy = row16_sum(sum_sq<SPL>(y));
@@ -1271,6 +1462,37 @@ KernelFn pick_anyh(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw) {
   }
 }
 
+template <int SPL, bool MASKED>
+KernelFn bank_fn(int nb) {
+  switch (nb) {
+#define ATTNRES_CASE(N) \
+  case N: return attnres_bank_kernel<SPL, MASKED, N>;
+    ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
+    ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
+#undef ATTNRES_CASE
+    default: return nullptr;
+  }
+}
+KernelFn pick_bank(const AnyShape &sh, int nb) {
+  if (sh.spl == 2) return sh.masked ? bank_fn<2, true>(nb) : bank_fn<2, false>(nb);
+  return sh.masked ? bank_fn<4, true>(nb) : bank_fn<4, false>(nb);
+}
+template <int SPL, bool MASKED, bool BANK>
+KernelFn cur_fn(bool d, bool o) {
+  if (d) return o ? attnres_cur_kernel<SPL, MASKED, true, true, BANK>
+                  : attnres_cur_kernel<SPL, MASKED, true, false, BANK>;
+  return o ? attnres_cur_kernel<SPL, MASKED, false, true, BANK>
+           : attnres_cur_kernel<SPL, MASKED, false, false, BANK>;
+}
+template <int SPL, bool MASKED>
+KernelFn cur_fn_b(bool d, bool o, bool bank) {
+  return bank ? cur_fn<SPL, MASKED, true>(d, o) : cur_fn<SPL, MASKED, false>(d, o);
+}
+KernelFn pick_cur(const AnyShape &sh, bool d, bool o, bool bank) {
+  if (sh.spl == 2) return sh.masked ? cur_fn_b<2, true>(d, o, bank) : cur_fn_b<2, false>(d, o, bank);
+  return sh.masked ? cur_fn_b<4, true>(d, o, bank) : cur_fn_b<4, false>(d, o, bank);
+}
+
 enum class Kind { kRow, kSplit, kAnyH };
 
 // Smallest call, in elements per row array (T * H), for which the row
@@ -1612,6 +1834,49 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
   return ATTNRES_OK;
 }
 
+// The two kernels of the two-kernel form.  Both take the whole call's
+// arguments (each validated as attnres_fwd would) and the partial-state
+// buffer; the bank part launches nothing without bank rows.
+int two_part_impl(const FwdArgs &a, const void *partial, int64_t partial_bytes, void *stream,
+                  bool bank_part) {
+  int rc = validate(a);
+  if (rc == ATTNRES_OK) rc = validate_partial(a, partial, partial_bytes);
+  if (rc != ATTNRES_OK) return rc;
+  if (a.T == 0 || (bank_part && a.num_blocks == 0)) return ATTNRES_OK;
+
+  KParams kp{};
+  kp.prefix = static_cast<uint16_t *>(const_cast<void *>(a.prefix));
+  kp.delta = static_cast<const uint16_t *>(a.delta);
+  kp.blocks = static_cast<uint16_t *>(const_cast<void *>(a.blocks));
+  kp.res_w = static_cast<const uint16_t *>(a.res_w);
+  kp.rms_w = static_cast<const uint16_t *>(a.rms_w);
+  kp.onw = static_cast<const uint16_t *>(a.output_norm_weight);
+  kp.out = static_cast<uint16_t *>(const_cast<void *>(a.out));
+  kp.tok_stride = a.block_token_stride;
+  kp.slot_stride = a.block_slot_stride;
+  kp.prefix_stride = row_stride(a.prefix_stride, a.T, a.H);
+  kp.delta_stride = a.delta ? row_stride(a.delta_stride, a.T, a.H) : 0;
+  kp.out_stride = row_stride(a.out_stride, a.T, a.H);
+  kp.nseg = int(a.H / kSeg);
+  kp.inv_h = 1.0f / float(a.H);
+  kp.rms_eps = a.rms_eps;
+  kp.out_eps = a.output_norm_weight ? a.output_norm_eps : 0.f;
+  kp.widx = a.block_write_idx;
+  kp.T = int(a.T);
+  kp.partial = static_cast<float *>(const_cast<void *>(partial));
+
+  const AnyShape sh = anyh_shape(a.H);
+  KernelFn fn = bank_part ? pick_bank(sh, a.num_blocks)
+                          : pick_cur(sh, a.delta != nullptr, a.output_norm_weight != nullptr,
+                                     a.num_blocks > 0);
+  if (!fn) return ATTNRES_E_NUM_BLOCKS;
+  void *args[] = {&kp};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(unsigned(a.T)),
+                                 dim3(unsigned(sh.threads)), args, 0,
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e);
+}
+
 FwdArgs make_args(const void *prefix, int64_t prefix_stride, const void *delta,
                   int64_t delta_stride, const void *blocks, int64_t ts, int64_t ss,
                   int max_blocks, int num_blocks, const void *res_w, const void *rms_w,
@@ -1696,6 +1961,40 @@ extern "C" int attnres_fwd_noalloc(void *prefix, int64_t prefix_stride, const vo
                             rms_w, rms_eps, output_norm_weight, output_norm_eps, block_write_idx,
                             out, out_stride, T, H),
                   stream, path, /*noalloc=*/true);
+}
+
+extern "C" int64_t attnres_partial_bytes(int64_t T, int64_t H) {
+  return attnres::partial_bytes(T, H);
+}
+
+extern "C" int attnres_fwd_bank(const void *prefix, int64_t prefix_stride, const void *delta,
+                                int64_t delta_stride, const void *blocks,
+                                int64_t block_token_stride, int64_t block_slot_stride,
+                                int max_blocks, int num_blocks, const void *res_w,
+                                const void *rms_w, float rms_eps, const void *output_norm_weight,
+                                float output_norm_eps, int block_write_idx, const void *out,
+                                int64_t out_stride, int64_t T, int64_t H, void *partial,
+                                int64_t partial_bytes, void *stream) {
+  return two_part_impl(make_args(prefix, prefix_stride, delta, delta_stride, blocks,
+                                 block_token_stride, block_slot_stride, max_blocks, num_blocks,
+                                 res_w, rms_w, rms_eps, output_norm_weight, output_norm_eps,
+                                 block_write_idx, out, out_stride, T, H),
+                       partial, partial_bytes, stream, /*bank_part=*/true);
+}
+
+extern "C" int attnres_fwd_cur(void *prefix, int64_t prefix_stride, const void *delta,
+                               int64_t delta_stride, void *blocks, int64_t block_token_stride,
+                               int64_t block_slot_stride, int max_blocks, int num_blocks,
+                               const void *res_w, const void *rms_w, float rms_eps,
+                               const void *output_norm_weight, float output_norm_eps,
+                               int block_write_idx, void *out, int64_t out_stride, int64_t T,
+                               int64_t H, const void *partial, int64_t partial_bytes,
+                               void *stream) {
+  return two_part_impl(make_args(prefix, prefix_stride, delta, delta_stride, blocks,
+                                 block_token_stride, block_slot_stride, max_blocks, num_blocks,
+                                 res_w, rms_w, rms_eps, output_norm_weight, output_norm_eps,
+                                 block_write_idx, out, out_stride, T, H),
+                       partial, partial_bytes, stream, /*bank_part=*/false);
 }
 
 extern "C" int attnres_init(int device) {

@@ -158,6 +158,41 @@ int validate(const FwdArgs &a) {
   return ATTNRES_OK;
 }
 
+int64_t partial_bytes(int64_t T, int64_t H) {
+  if (T < 0 || T > kMaxTokens || H <= 0) return ATTNRES_E_SHAPE;
+  if (H % 8 != 0 || H > kMaxHidden) return ATTNRES_E_UNSUPPORTED;
+  return 4 * T * H + 8 * T;  // fp32 [T, H], then (m, s) per token
+}
+
+int validate_partial(const FwdArgs &a, const void *partial, int64_t bytes) {
+  if (a.T == 0 || a.num_blocks == 0) return ATTNRES_OK;
+  if (!partial) return ATTNRES_E_NULL;
+  if (!aligned16(partial)) return ATTNRES_E_ALIGN;
+  const int64_t need = partial_bytes(a.T, a.H);
+  if (need < 0) return int(need);
+  if (bytes < need) return ATTNRES_E_SHAPE;
+  // Written by the bank part and read by the cur part: it must not share a
+  // byte with any argument.
+  const Rows w = rows(partial, 1, 0, need, true);
+  const bool bank_used = a.num_blocks > 0 || a.block_write_idx >= 0;
+  const i128 row_bytes = 2 * static_cast<i128>(a.H);
+  auto mat = [&](const void *p, int64_t stride) {
+    return rows(p, a.T, 2 * static_cast<i128>(row_stride(stride, a.T, a.H)), row_bytes, false);
+  };
+  i128 bank_bytes = 0;
+  if (bank_used)
+    bank_bytes = 2 * (static_cast<i128>(a.T - 1) * a.block_token_stride +
+                      static_cast<i128>(a.max_blocks - 1) * a.block_slot_stride + a.H);
+  const Rows r[7] = {
+      mat(a.prefix, a.prefix_stride), mat(a.delta, a.delta_stride),
+      rows(bank_used ? a.blocks : nullptr, 1, 0, bank_bytes, false),
+      rows(a.res_w, 1, 0, row_bytes, false), rows(a.rms_w, 1, 0, row_bytes, false),
+      rows(a.output_norm_weight, 1, 0, row_bytes, false), mat(a.out, a.out_stride)};
+  for (const Rows &x : r)
+    if (overlap(w, x)) return ATTNRES_E_ALIAS;
+  return ATTNRES_OK;
+}
+
 const char *strerror_text(int status) {
   switch (status) {
     case ATTNRES_OK: return "ok";

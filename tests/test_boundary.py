@@ -299,3 +299,41 @@ def test_plain_c_caller_builds_and_links():
         pytest.skip("a GPU is present: the run is covered by the GPU test")
     res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert res.returncode == 2, res.stdout + res.stderr
+
+
+def test_partial_bytes(A):
+    """The two-kernel form's state: fp32 [T, H] plus two fp32 per token."""
+    lib = A.lib()
+    assert lib.attnres_partial_bytes(1, H) == 4 * H + 8
+    assert lib.attnres_partial_bytes(1024, 5120) == 4 * 1024 * 5120 + 8 * 1024
+    assert lib.attnres_partial_bytes(0, H) == 0
+    assert A.STATUS[lib.attnres_partial_bytes(-1, H)] == "ATTNRES_E_SHAPE"
+    assert A.STATUS[lib.attnres_partial_bytes(4, 7164)] == "ATTNRES_E_UNSUPPORTED"
+
+
+def _two_part_rc(A, fn_name, a, partial, nbytes):
+    return getattr(A.lib(), fn_name)(
+        a["prefix"], a["H"], a["delta"], a["H"], a["blocks"], a["ts"], a["ss"], a["cap"], a["nb"],
+        a["res_w"], a["rms_w"], a["eps"], a["onw"], a["oeps"], a["widx"], a["out"], a["H"], a["T"],
+        a["H"], partial, nbytes, None)
+
+
+@pytest.mark.parametrize("fn_name", ["attnres_fwd_bank", "attnres_fwd_cur"])
+def test_two_kernel_form_rejects_before_any_gpu_work(A, fn_name):
+    """Both halves check the whole call as attnres_fwd does, then the partial
+    buffer, and return the code without touching the (fake) pointers."""
+    a = _args()
+    need = A.lib().attnres_partial_bytes(a["T"], H)
+    part = 0x60000000
+    assert A.STATUS[_two_part_rc(A, fn_name, _args(H=7164), part, need)] == "ATTNRES_E_UNSUPPORTED"
+    assert A.STATUS[_two_part_rc(A, fn_name, a, None, need)] == "ATTNRES_E_NULL"
+    assert A.STATUS[_two_part_rc(A, fn_name, a, part + 8, need)] == "ATTNRES_E_ALIGN"
+    assert A.STATUS[_two_part_rc(A, fn_name, a, part, need - 16)] == "ATTNRES_E_SHAPE"
+    # overlapping the output, the bank or a weight
+    for other in ("out", "blocks", "res_w"):
+        assert A.STATUS[_two_part_rc(A, fn_name, a, a[other], need)] == "ATTNRES_E_ALIAS", other
+    # no bank rows: no buffer needed, so these get as far as the launch (only
+    # the bank half, which then launches nothing, returns OK without a GPU)
+    if fn_name == "attnres_fwd_bank":
+        assert A.STATUS[_two_part_rc(A, fn_name, _args(nb=0, blocks=None), None, 0)] == "ATTNRES_OK"
+    assert A.STATUS[_two_part_rc(A, fn_name, _args(T=0, prefix=None, out=None), None, 0)] == "ATTNRES_OK"
