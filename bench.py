@@ -383,6 +383,43 @@ def _host_threads() -> int:
 HIDDEN_SWEEP = (2048, 2880, 4096, 5120, 7168, 8192, 12288, 16384)
 
 
+def anyh_threads(H: int) -> int:
+    """Lanes per workgroup of the library's any-H kernel at hidden size H:
+    whole waves of two segments per lane up to 1024 segments, else four."""
+    nseg = H // 8
+    spl = 2 if nseg <= 1024 else 4
+    return -(-nseg // (64 * spl)) * 64
+
+
+def probe_mid_h(H: int, T: int, cached: bool, steps: int = 120):
+    """The traffic probe of the mid-prefill pattern at hidden size H in the
+    any-H kernel's launch shape: us per call (graph replay over enough
+    buffers to exceed the Infinity Cache)."""
+    lib = load_ceiling_probe()
+    per_set = 2 * H * T * 11
+    sets = []
+    for _ in range(max(2, -(-2 * MALL_BYTES // per_set))):
+        sets.append(tuple(torch.randint(-30000, 30000, (n * H,), dtype=torch.int16, device="cuda")
+                          for n in (T * 8, T, T)) + (torch.empty(T * H, dtype=torch.int16,
+                                                                 device="cuda"),))
+
+    def call(st):
+        rc = lib.ceiling_mid_h(st[0].data_ptr(), st[1].data_ptr(), st[2].data_ptr(),
+                               st[3].data_ptr(), T, H, anyh_threads(H), int(cached),
+                               torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"ceiling_mid_h failed ({rc})")
+
+    calls = [lambda st=st: call(st) for st in sets]
+    for fn in calls:
+        fn()
+    torch.cuda.synchronize()
+    t = time_graph(calls, steps, replays=3, min_calls=MIN_TIMED_CALLS)
+    del sets
+    torch.cuda.empty_cache()
+    return pct([x / steps * 1e3 for x in t], 50)
+
+
 def bench_hidden_sweep(Hs=HIDDEN_SWEEP, T: int = 1024, steps: int = 120):
     """The mid-prefill recipe (T=1024, 8 block rows, delta, output norm,
     block_write_idx=3) at other hidden sizes, run by the any-H row kernel
@@ -410,9 +447,17 @@ def bench_hidden_sweep(Hs=HIDDEN_SWEEP, T: int = 1024, steps: int = 120):
             entry[name] = dict(us=round(us, 2), GBps=round(gbps, 1),
                                frac=round(gbps / HBM_PEAK_GBPS, 4))
             log(f"hidden sweep H={H} {name}: {us:.2f} us, {gbps:.0f} GB/s")
-        res[str(H)] = entry
         del sets
         torch.cuda.empty_cache()
+        # The same rows moved with no arithmetic, in the any-H launch shape and
+        # the cache policy the kernel uses for this size.
+        cached = T * H >= 1024 * 7168
+        pus = probe_mid_h(H, T, cached)
+        entry["traffic_probe"] = dict(us=round(pus, 2), cached_rewritten_rows=cached,
+                                      frac=round(nbytes / pus / 1e3 / HBM_PEAK_GBPS, 4),
+                                      any_h_fraction_of_probe=round(pus / entry["any_h"]["us"], 4))
+        log(f"hidden sweep H={H} probe: {pus:.2f} us")
+        res[str(H)] = entry
     return res
 
 
@@ -527,6 +572,8 @@ def load_ceiling_probe():
     lib.ceiling_stream.argtypes = [vp, i64, vp, i64, ci, ci, ci, i64, u32, vp]
     lib.ceiling_mid.argtypes = [vp, vp, vp, vp, i64, ci, vp]
     lib.ceiling_mid.restype = ci
+    lib.ceiling_mid_h.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, vp]
+    lib.ceiling_mid_h.restype = ci
     lib.ceiling_stream.restype = ci
     return lib
 
@@ -967,6 +1014,14 @@ def main():
         return
     if args.configs:
         table = bench_configs()
+        # The rows of the (nb=8, delta, norm, write slot 7) cases moved with no
+        # arithmetic, in the row kernel's launch shape and cache policy.
+        probes = {}
+        for T in (256, 2048):
+            pus = probe_mid_h(W.HIDDEN, T, T * W.HIDDEN >= 1024 * 7168)
+            nbytes = W.Case("p", T=T, nb=8, widx=7).algorithmic_bytes()
+            probes[f"T{T}"] = dict(us=round(pus, 3), frac=round(nbytes / pus / 1e3 / HBM_PEAK_GBPS, 4))
+            log(f"configs: traffic probe T={T}: {pus:.2f} us")
         print(json.dumps({"metric": "attention-residual forward latency and throughput per case",
                           "unit": "us/call", "higher_is_better": False, "data": "synthetic",
                           "config": {"workload": "the reference case (T=4, nb=4, delta, output "
@@ -974,7 +1029,8 @@ def main():
                                                  "nb 0/4/8 x delta x output norm x write slot "
                                                  "-1/nb-1), H=7168, bf16",
                                      "timing": "hipGraph replay, rotating token windows"},
-                          "cases": table, "kernel_source_hash": kernel_source_hash()}),
+                          "cases": table, "traffic_probe_nb8_delta_norm_w7": probes,
+                          "kernel_source_hash": kernel_source_hash()}),
               flush=True)
         return
     if args.variant_sweep:

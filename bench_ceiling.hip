@@ -94,6 +94,58 @@ __global__ void __launch_bounds__(kThreads) mid_kernel(u32x4 *bank, u32x4 *prefi
   }
 }
 
+// The mid-prefill pattern of mid_kernel for any hidden size: nseg 16-byte
+// segments per row, the library's any-H launch shape (blockDim.x lanes of
+// SPL segments each, lane + i * blockDim.x, segments past the row end masked).
+template <int SPL, bool CACHED>
+__global__ void __launch_bounds__(512) mid_any_kernel(u32x4 *bank, u32x4 *prefix,
+                                                      const u32x4 *delta, u32x4 *out, int nseg) {
+  const int64_t t = blockIdx.x;
+  u32x4 *bk = bank + t * 8 * nseg;
+  u32x4 *pf = prefix + t * nseg;
+  const u32x4 *dl = delta + t * nseg;
+  u32x4 *o = out + t * nseg;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto ldc = [&](const u32x4 *row, int seg) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(row), 0, nseg * 16, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, seg * 16, 0, 0);
+  };
+  u32x4 x[10][SPL];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int seg = threadIdx.x + i * blockDim.x;
+      if (CACHED && r == kMidSlot)  // the buffer load masks the row end itself
+        x[r][i] = ldc(bk + r * nseg, seg);
+      else
+        x[r][i] = seg < nseg ? ld(bk + r * nseg + seg) : zero;
+    }
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int seg = threadIdx.x + i * blockDim.x;
+    if (CACHED)
+      x[8][i] = ldc(pf, seg);
+    else
+      x[8][i] = seg < nseg ? ld(pf + seg) : zero;
+    x[9][i] = seg < nseg ? ld(dl + seg) : zero;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int seg = threadIdx.x + i * blockDim.x;
+    if (seg >= nseg) continue;
+    u32x4 acc = x[0][i];
+#pragma unroll
+    for (int r = 1; r < 10; ++r) acc ^= x[r][i];
+    const u32x4 cur = x[8][i] ^ x[9][i];
+    st(o + seg, acc);
+    st(pf + seg, cur);
+    st(bk + kMidSlot * nseg + seg, cur);
+  }
+}
+
 template <int R, int WD, int WI>
 __global__ void __launch_bounds__(kThreads) ceiling_kernel(u32x4 *src, int64_t src_stride,
                                                            u32x4 *dst, int64_t dst_stride,
@@ -180,5 +232,31 @@ extern "C" int ceiling_stream(void *src, int64_t src_token_stride, void *dst,
   void *args[] = {&args_src, &ss, &args_dst, &ds, &never};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(unsigned(T)),
                                  dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : -2;
+}
+
+// The mid-prefill layout at hidden size H (a multiple of 8, at most 16384),
+// `threads` lanes per workgroup (a multiple of 64, at most 512) with two (H
+// up to 8192) or four segments per lane covering the row.  Returns 0 on
+// success, -1 for bad arguments, -2 if the launch failed.
+extern "C" int ceiling_mid_h(void *bank, void *prefix, const void *delta, void *out, int64_t T,
+                             int64_t H, int threads, int cached, void *stream) {
+  if (T < 0 || T > 0x7fffffff || H <= 0 || H % 8 != 0 || H > 16384) return -1;
+  if (threads <= 0 || threads > 512 || threads % 64 != 0) return -1;
+  if (T == 0) return 0;
+  if (!bank || !prefix || !delta || !out) return -1;
+  if (!aligned16(bank) || !aligned16(prefix) || !aligned16(delta) || !aligned16(out)) return -1;
+  int nseg = int(H / 8);
+  const int spl = nseg <= 1024 ? 2 : 4;
+  if (int64_t(threads) * spl < nseg) return -1;
+  void *a_bank = bank, *a_prefix = prefix, *a_delta = const_cast<void *>(delta), *a_out = out;
+  void *args[] = {&a_bank, &a_prefix, &a_delta, &a_out, &nseg};
+  const void *fn =
+      spl == 2 ? (cached ? reinterpret_cast<const void *>(mid_any_kernel<2, true>)
+                         : reinterpret_cast<const void *>(mid_any_kernel<2, false>))
+               : (cached ? reinterpret_cast<const void *>(mid_any_kernel<4, true>)
+                         : reinterpret_cast<const void *>(mid_any_kernel<4, false>));
+  hipError_t e = hipLaunchKernel(fn, dim3(unsigned(T)), dim3(unsigned(threads)), args, 0,
+                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? 0 : -2;
 }

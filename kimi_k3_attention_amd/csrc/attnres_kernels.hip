@@ -142,6 +142,8 @@ struct KParams {
   int widx;
   int T;
   int nseg;               // segments per row (H / 8); the any-H kernel's row length
+  int threads;            // lanes per workgroup of the any-H launch shape (a kernel
+                          // argument: blockDim.x would be read with a vector load)
   float inv_h;            // 1 / H
   uint64_t *ws_part;       // split path: tagged words, 14 parts per token
   unsigned *ws_flag;
@@ -239,13 +241,38 @@ __device__ __forceinline__ float lane_shuffle(float v, int src) {
 // no prefix, delta or cur.  Q: load the scoring weights for the fused query
 // (needed whenever a logit is formed: with bank rows, or in the second
 // kernel of the two-kernel form, which scores cur alone).
+//
+// LR > 0: the first LR sources (bank rows) go straight from memory into LDS
+// (global_load_lds, 16 bytes per lane, no registers), issued after every
+// other row; they are read back from LDS when used.  That frees 4 SPL
+// registers per row, so more workgroups fit a CU (see the any-H kernel).
 template <int NB, bool DELTA, bool ONORM, int SPL, bool MASKED = false, bool CACHE_RW = false,
-          bool CUR = true, bool Q = (NB > 0)>
+          bool CUR = true, bool Q = (NB > 0), int LR = 0>
 struct Token {
   static constexpr int NS = NB + (CUR ? 1 : 0);
+  static_assert(LR == 0 || (CUR && LR < NB), "LDS rows are bank rows of a full token");
   u32x4 rms[SPL], res[SPL], onw[SPL];  // weights
   u32x4 x[NB + 1][SPL];                // bank slots 0..NB-1, then prefix (cur after finish_cur)
   u32x4 d[SPL];                        // delta
+  u32x4 *lds_rows = nullptr;           // LR > 0: [LR][SPL][lanes] in LDS
+  int nthr = 0;                        // lanes per workgroup (LR > 0)
+  bool seg_ok[SPL];
+
+  // Source j, segment i: from LDS for the first LR sources (zero past a
+  // masked row's end), else from registers.
+  __device__ __forceinline__ u32x4 row(int j, int i) const {
+    if (j < LR) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const u32x4 v = lds_rows[(j * SPL + i) * nthr + int(threadIdx.x)];
+      return MASKED && !seg_ok[i] ? zero : v;
+    }
+    return x[j][i];
+  }
+  // The LDS rows are written by the memory system behind the compiler's
+  // back: wait for every load in flight before reading them.
+  __device__ __forceinline__ static void wait_lds_rows() {
+    if constexpr (LR > 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
 
   __device__ __forceinline__ static bool in_row(const KParams &p, int seg) {
     return !MASKED || seg < p.nseg;
@@ -298,6 +325,7 @@ struct Token {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
       ok[i] = in_row(p, seg0 + i * seg_step);
+      seg_ok[i] = ok[i];
       sb[i] = seg_bytes(seg0, seg_step, i);
     }
     if constexpr (Q)  // a single source needs no logit, hence no query
@@ -329,7 +357,7 @@ struct Token {
       // in flight, and every source's arithmetic would wait for all of them.
       static_assert(NB > 0, "a rewritten source row needs a source slot");
 #pragma unroll
-      for (int k = 0; k + 1 < NB; ++k) {
+      for (int k = LR; k + 1 < NB; ++k) {
         const int slot = k + (k >= p.widx ? 1 : 0);
         const uint16_t *row = bank + slot * p.slot_stride;
 #pragma unroll
@@ -354,7 +382,7 @@ struct Token {
       // them by when their addresses are ready), so that the partials of each
       // source can start as soon as its own rows land.
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
+      for (int j = LR; j < NB; ++j) {
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
           x[j][i] = load_row(at(bank + j * p.slot_stride, sb[i]), ok[i]);
@@ -367,6 +395,26 @@ struct Token {
 #pragma unroll
       for (int i = 0; i < SPL; ++i)
         d[i] = load_row(at(p.delta + t * p.delta_stride, sb[i]), ok[i]);
+    if constexpr (LR > 0) {
+      // The first LR sources last, straight into LDS: in the cached variant
+      // the first LR of the ascending slots other than widx, else slots
+      // 0..LR-1.  Each wave writes 64 consecutive 16-byte slots.
+      __builtin_amdgcn_sched_barrier(0);
+      const int wave_base = int(threadIdx.x) & ~(kWave - 1);
+#pragma unroll
+      for (int k = 0; k < LR; ++k) {
+        const int slot = CACHE_RW ? k + (k >= p.widx ? 1 : 0) : k;
+        const uint16_t *rowp = bank + slot * p.slot_stride;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+          u32x4 *dst = lds_rows + (k * SPL + i) * nthr + wave_base;
+          if (!MASKED || ok[i])
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)at(rowp, sb[i]),
+                (__attribute__((address_space(3))) void *)dst, 16, 0, ATTNRES_NT_LOADS ? 2 : 0);
+        }
+      }
+    }
     // Keep the scheduler from sinking any of these loads below the arithmetic.
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -418,13 +466,15 @@ struct Token {
                                           float &ss, float &dq) const {
     float s = 0.f, dd = 0.f;
 #pragma unroll
-    for (int i = 0; i < SPL; ++i)
+    for (int i = 0; i < SPL; ++i) {
+      const u32x4 v = row(j, i);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        s = dot2(x[j][i][k], x[j][i][k], s);
-        dd = dot2(qh[i][k], x[j][i][k], dd);
-        dd = dot2(ql[i][k], x[j][i][k], dd);
+        s = dot2(v[k], v[k], s);
+        dd = dot2(qh[i][k], v[k], dd);
+        dd = dot2(ql[i][k], v[k], dd);
       }
+    }
     ss = s;
     dq = dd;
   }
@@ -441,7 +491,7 @@ struct Token {
   // copies.  Emits no instruction.
   __device__ __forceinline__ void keep_packed() {
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
+    for (int j = LR; j < NS; ++j)
 #pragma unroll
       for (int i = 0; i < SPL; ++i) asm volatile("" : "+v"(x[j][i]));
   }
@@ -470,26 +520,30 @@ struct Token {
       const uint32_t ph = (wa & 0xffffu) | (wb << 16);          // (pa_hi, pb_hi)
       const uint32_t pl = (wa >> 16) | (wb & 0xffff0000u);      // (pa_lo, pb_lo)
 #pragma unroll
-      for (int i = 0; i < SPL; ++i)
+      for (int i = 0; i < SPL; ++i) {
+        const u32x4 va = row(a, i), vb = row(a + 1, i);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           // {S0 = x_b, S1 = x_a}: bytes 0-3 are x_a's, 4-7 x_b's
-          const uint32_t lo2 = __builtin_amdgcn_perm(x[a + 1][i][k], x[a][i][k], 0x05040100u);
-          const uint32_t hi2 = __builtin_amdgcn_perm(x[a + 1][i][k], x[a][i][k], 0x07060302u);
+          const uint32_t lo2 = __builtin_amdgcn_perm(vb[k], va[k], 0x05040100u);
+          const uint32_t hi2 = __builtin_amdgcn_perm(vb[k], va[k], 0x07060302u);
           y[i][2 * k] = dot2(pl, lo2, dot2(ph, lo2, y[i][2 * k]));
           y[i][2 * k + 1] = dot2(pl, hi2, dot2(ph, hi2, y[i][2 * k + 1]));
         }
+      }
     }
     if constexpr (NS % 2 == 1) {
       constexpr int j = NS - 1;
       const float pj = lane_value(p_lane, j);
 #pragma unroll
-      for (int i = 0; i < SPL; ++i)
+      for (int i = 0; i < SPL; ++i) {
+        const u32x4 v = row(j, i);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          y[i][2 * k] = fmaf(pj, bf_lo(x[j][i][k]), y[i][2 * k]);
-          y[i][2 * k + 1] = fmaf(pj, bf_hi(x[j][i][k]), y[i][2 * k + 1]);
+          y[i][2 * k] = fmaf(pj, bf_lo(v[k]), y[i][2 * k]);
+          y[i][2 * k + 1] = fmaf(pj, bf_hi(v[k]), y[i][2 * k + 1]);
         }
+      }
     }
   }
 
@@ -759,21 +813,28 @@ constexpr int kAnyMaxRows = kAnyMaxThreads / 16;  // 16-lane row partials per wo
 // fixed order.  All kAnyMaxRows / 4 groups of the row are read at once (the
 // row always holds that many, so the reads stay in bounds) and the groups
 // past n4 count as zero.
+// CHUNK: float4 reads issued together (fewer hold fewer registers while the
+// rows are live; the sum is the same).
+template <int CHUNK = kAnyMaxRows / 4>
 __device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
   constexpr int kMax4 = kAnyMaxRows / 4;
+  static_assert(kMax4 % CHUNK == 0, "whole chunks");
   const float4 *v4 = reinterpret_cast<const float4 *>(v);
-  float4 a[kMax4];
-#pragma unroll
-  for (int i = 0; i < kMax4; ++i) a[i] = v4[i];
-  __builtin_amdgcn_sched_barrier(0);
   float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMax4; ++i) {
-    if (i < n4) {
-      sx += a[i].x;
-      sy += a[i].y;
-      sz += a[i].z;
-      sw += a[i].w;
+  for (int c = 0; c < kMax4; c += CHUNK) {
+    float4 a[CHUNK];
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) a[i] = v4[c + i];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i) {
+      if (c + i < n4) {
+        sx += a[i].x;
+        sy += a[i].y;
+        sz += a[i].z;
+        sw += a[i].w;
+      }
     }
   }
   return (sx + sy) + (sz + sw);
@@ -783,15 +844,22 @@ __device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
 // (whole waves, at most kAnyMaxThreads) with SPL segments each, blockDim.x *
 // SPL >= p.nseg.  With two segments per lane a token fits 128 VGPRs (four
 // waves per SIMD); four segments may take 256.
-template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false>
+//
+// LR > 0 (kAnyLdsRows bank rows in LDS, launched with LR * SPL * blockDim.x
+// * 16 bytes of dynamic LDS): the same steps with those rows held in LDS
+// instead of registers, for one more resident workgroup per CU where the
+// registers are what limits it (see anyh_lds_rows).
+template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, int LR = 0>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWave, kAnyMaxThreads),
-                               amdgpu_waves_per_eu(SPL <= 2 ? 4 : 2)))
+                               amdgpu_waves_per_eu(LR == 0 ? (SPL <= 2 ? 4 : 2)
+                                                           : (SPL <= 2 ? 5 : 3))))
 attnres_anyh_kernel(KParams p) {
   constexpr int NS = NB + 1;
   __shared__ __align__(16) float s_part[2 * NS][kAnyMaxRows];
   __shared__ __align__(16) float s_ysq[kAnyMaxRows];
+  extern __shared__ __align__(16) u32x4 s_rows[];
 
-  const int nthreads = blockDim.x;
+  const int nthreads = p.threads;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rowslot = wave * 4 + (lane >> 4);
@@ -801,7 +869,9 @@ attnres_anyh_kernel(KParams p) {
   const int seg0 = int(threadIdx.x);  // whole-line loads, as in the row kernel
   const int seg_step = nthreads;
 
-  Token<NB, DELTA, ONORM, SPL, MASKED, CACHE_RW> tk;
+  Token<NB, DELTA, ONORM, SPL, MASKED, CACHE_RW, true, (NB > 0), LR> tk;
+  tk.lds_rows = s_rows;
+  tk.nthr = p.threads;
   tk.issue(p, t, seg0, seg_step);
   if constexpr (NB == 0) {
     // One source, weight exactly 1 (as in the row kernel).
@@ -822,17 +892,20 @@ attnres_anyh_kernel(KParams p) {
   u32x4 qh[SPL], ql[SPL];
   tk.query(qh, ql);
 
-  // Each source's partials as its rows land, cur last (as in the row kernel).
+  // Each source's partials as its rows land, cur last (as in the row kernel);
+  // then the LDS rows, issued last, once every load has landed.
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
+  for (int j = LR; j < NS + LR; ++j) {
+    const int src = j < NS ? j : j - NS;
     if (j == NB) tk.finish_cur();
+    if (j == NS) tk.wait_lds_rows();
     float sj, dj;
-    tk.partial(j, qh, ql, sj, dj);
+    tk.partial(src, qh, ql, sj, dj);
     sj = row16_sum(sj);
     dj = row16_sum(dj);
     if (row_leader) {
-      s_part[j][rowslot] = sj;
-      s_part[NS + j][rowslot] = dj;
+      s_part[src][rowslot] = sj;
+      s_part[NS + src][rowslot] = dj;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -842,7 +915,9 @@ attnres_anyh_kernel(KParams p) {
 
   // Lane j < NS sums source j's squares, lane 32 + j its query dots.
   float tot = 0.f;
-  if ((lane & 31) < NS) tot = sum_row_partials_n(s_part[(lane & 31) + (lane >> 5) * NS], n4);
+  if ((lane & 31) < NS)
+    tot = sum_row_partials_n<LR == 0 ? kAnyMaxRows / 4 : kAnyMaxRows / 16>(
+        s_part[(lane & 31) + (lane >> 5) * NS], n4);
   const float dq_j = lane_shuffle(tot, (lane + 32) & (kWave - 1));
   const float logit = lane < NS ? dq_j * rsqrtf(tot * p.inv_h + p.rms_eps) : 0.f;
   const float p_lane = softmax_lanes<NS>(logit);
@@ -880,7 +955,7 @@ attnres_bank_kernel(KParams p) {
   static_assert(NB > 0, "the bank part needs bank rows");
   __shared__ __align__(16) float s_part[2 * NB][kAnyMaxRows];
 
-  const int nthreads = blockDim.x;
+  const int nthreads = p.threads;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rowslot = wave * 4 + (lane >> 4);
@@ -944,7 +1019,7 @@ attnres_cur_kernel(KParams p) {
   __shared__ __align__(16) float s_part[2][kAnyMaxRows];
   __shared__ __align__(16) float s_ysq[kAnyMaxRows];
 
-  const int nthreads = blockDim.x;
+  const int nthreads = p.threads;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rowslot = wave * 4 + (lane >> 4);
@@ -1444,6 +1519,64 @@ KernelFn anyh_fn(bool d, bool o, bool cache_rw) {
            : attnres_anyh_kernel<SPL, MASKED, NB, false, false>;
 }
 
+// The any-H kernel with kAnyLdsRows bank rows in LDS (4..8 bank rows).
+constexpr int kAnyLdsRows = 3;
+template <int SPL, bool MASKED, int NB>
+KernelFn anyh_lds_fn(bool d, bool o, bool c) {
+  if constexpr (NB >= 4) {
+    if (c) {
+      if (d)
+        return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, true, kAnyLdsRows>
+                 : attnres_anyh_kernel<SPL, MASKED, NB, true, false, true, kAnyLdsRows>;
+      return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, true, kAnyLdsRows>
+               : attnres_anyh_kernel<SPL, MASKED, NB, false, false, true, kAnyLdsRows>;
+    }
+    if (d)
+      return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, false, kAnyLdsRows>
+               : attnres_anyh_kernel<SPL, MASKED, NB, true, false, false, kAnyLdsRows>;
+    return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, false, kAnyLdsRows>
+             : attnres_anyh_kernel<SPL, MASKED, NB, false, false, false, kAnyLdsRows>;
+  }
+  return nullptr;
+}
+template <int NB>
+KernelFn anyh_lds_pick(const AnyShape &sh, bool d, bool o, bool c) {
+  if (sh.spl != 2) return nullptr;
+  return sh.masked ? anyh_lds_fn<2, true, NB>(d, o, c) : anyh_lds_fn<2, false, NB>(d, o, c);
+}
+KernelFn pick_anyh_lds(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw) {
+  switch (nb) {
+#define ATTNRES_CASE(N) \
+  case N: return anyh_lds_pick<N>(sh, d, o, cache_rw);
+    ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
+#undef ATTNRES_CASE
+    default: return nullptr;
+  }
+}
+
+// Whether an any-H call holds kAnyLdsRows bank rows in LDS, and the dynamic
+// LDS bytes it then takes.  Registers bound the resident workgroups per CU of
+// the plain kernel: at two segments per lane it may take 128 VGPRs (four
+// waves per SIMD), so three 5-wave workgroups fit (H = 4104..5120), and a
+// call of more tokens than that runs a partial second round (T = 1024 at
+// H = 5120: 768 + 256).  With three bank rows out of the registers the kernel
+// is built for 96 VGPRs and four fit, 1024 per round.  The rows then take
+// 30 KB of LDS per workgroup (4 x 32 KB of a CU's 160 KB).  Its cost: with
+// loads into LDS in flight the compiler waits for every load before the first
+// arithmetic, so no source's arithmetic overlaps the later rows' arrival.
+// Measured (T = 1024, delta and norm, µs per call, plain / LDS rows): H = 5120
+// nb = 5 22.6 / 20.4, nb = 7 26.6 / 23.2, nb = 8 28.8 / 27.0; where the extra
+// workgroup did not change the rounds it lost: H = 6144 (6 waves, two to four
+// per CU) nb = 6 27.5 / 30.3, H = 10240 and 12288 (four segments, one to two
+// per CU) +11-13 %.  So only 5-wave workgroups with 4 or more bank rows, and
+// only when the tokens exceed the plain kernel's three per CU.
+bool anyh_lds_rows(const AnyShape &sh, int64_t T, int nb, int cus, size_t *dyn) {
+  const int waves = sh.threads / kWave;
+  if (sh.spl != 2 || waves != 5 || nb < 4 || T <= int64_t(3) * cus) return false;
+  *dyn = size_t(kAnyLdsRows) * sh.spl * sh.threads * 16;
+  return true;
+}
+
 template <int NB>
 KernelFn anyh_pick(const AnyShape &sh, bool d, bool o, bool c) {
   if (sh.spl == 2)
@@ -1700,6 +1833,25 @@ int compute_units(int dev, int *cus) {
 
 // noalloc: the split path takes the static scratch instead of the allocated
 // workspace, and no stream hand-off is made (calls that overlap race).
+// Lets a kernel of the LDS-row variant take its dynamic LDS beyond the
+// default limit, once per kernel.  Where the runtime has no such limit the
+// attribute may be refused; the launch's own status then decides.
+std::mutex g_lds_attr_mu;
+const void *g_lds_attr_done[256];
+void allow_dynamic_lds(KernelFn fn, size_t bytes) {
+  const void *f = reinterpret_cast<const void *>(fn);
+  std::lock_guard<std::mutex> lock(g_lds_attr_mu);
+  for (const void *d : g_lds_attr_done)
+    if (d == f) return;
+  if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes)) != hipSuccess)
+    (void)hipGetLastError();
+  for (const void *&d : g_lds_attr_done)
+    if (d == nullptr) {
+      d = f;
+      break;
+    }
+}
+
 int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
   if (path != ATTNRES_PATH_AUTO && path != ATTNRES_PATH_ROW && path != ATTNRES_PATH_SPLIT &&
       path != ATTNRES_PATH_ANY_H)
@@ -1799,11 +1951,25 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
   hipError_t e;
   if (any_h) {
     const AnyShape sh = anyh_shape(a.H);
-    KernelFn fn = pick_anyh(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
+    kp.threads = sh.threads;
+    int cus = 0;
+    rc = compute_units(dev, &cus);
+    if (rc != ATTNRES_OK) return rc;
+    size_t dyn = 0;
+    KernelFn fn = nullptr;
+    if (anyh_lds_rows(sh, a.T, a.num_blocks, cus, &dyn)) {
+      fn = pick_anyh_lds(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
+      // the largest LDS this kernel takes: at the most lanes of its shape
+      if (fn) allow_dynamic_lds(fn, size_t(kAnyLdsRows) * sh.spl * 384 * 16);
+    }
+    if (!fn) {
+      dyn = 0;
+      fn = pick_anyh(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
+    }
     if (!fn) return ATTNRES_E_NUM_BLOCKS;
     void *args[] = {&kp};
     e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(unsigned(a.T)),
-                        dim3(unsigned(sh.threads)), args, 0, s);
+                        dim3(unsigned(sh.threads)), args, dyn, s);
     return e == hipSuccess ? ATTNRES_OK : hip_fail(e);
   }
 
@@ -1866,6 +2032,7 @@ int two_part_impl(const FwdArgs &a, const void *partial, int64_t partial_bytes, 
   kp.partial = static_cast<float *>(const_cast<void *>(partial));
 
   const AnyShape sh = anyh_shape(a.H);
+  kp.threads = sh.threads;
   KernelFn fn = bank_part ? pick_bank(sh, a.num_blocks)
                           : pick_cur(sh, a.delta != nullptr, a.output_norm_weight != nullptr,
                                      a.num_blocks > 0);

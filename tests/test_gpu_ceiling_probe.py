@@ -96,3 +96,38 @@ def test_mid_probe_moves_every_row(cached):
     assert (pf.view(np.uint32).reshape(T, H // 2) == cur).all()
     assert (bank.view(np.uint32).reshape(T, 8, H // 2) == want_bank).all()
     assert (dl == dl_h).all()
+
+
+@pytest.mark.parametrize("Hx,cached", [(5120, 0), (2888, 1), (12288, 0), (16376, 1)])
+def test_mid_probe_any_hidden_size(Hx, cached):
+    """The any-H mid-prefill probe (the library's any-H launch shape, row ends
+    masked) reads every row and writes out, prefix and bank slot 3 only."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bench
+    lib = bench.load_ceiling_probe()
+    T = 5
+    rng = np.random.default_rng(Hx + cached)
+    bank_h = rng.integers(0, 1 << 16, size=T * 8 * Hx, dtype=np.uint16)
+    pf_h = rng.integers(0, 1 << 16, size=T * Hx, dtype=np.uint16)
+    dl_h = rng.integers(0, 1 << 16, size=T * Hx, dtype=np.uint16)
+    out_h = np.full(T * Hx, 0x7F85, dtype=np.uint16)
+    dev = [torch.from_numpy(a.view(np.int16)).cuda() for a in (bank_h, pf_h, dl_h, out_h)]
+    rc = lib.ceiling_mid_h(dev[0].data_ptr(), dev[1].data_ptr(), dev[2].data_ptr(),
+                           dev[3].data_ptr(), T, Hx, bench.anyh_threads(Hx), cached,
+                           torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    bank, pf, dl, out = (d.cpu().numpy().view(np.uint16) for d in dev)
+    n = Hx // 2
+    b = bank_h.view(np.uint32).reshape(T, 8, n)
+    p32 = pf_h.view(np.uint32).reshape(T, n)
+    d32 = dl_h.view(np.uint32).reshape(T, n)
+    cur = p32 ^ d32
+    want_bank = b.copy()
+    want_bank[:, 3] = cur
+    assert (out.view(np.uint32).reshape(T, n) == np.bitwise_xor.reduce(b, axis=1) ^ p32 ^ d32).all()
+    assert (pf.view(np.uint32).reshape(T, n) == cur).all()
+    assert (bank.view(np.uint32).reshape(T, 8, n) == want_bank).all()
+    assert (dl == dl_h).all()
+    assert lib.ceiling_mid_h(None, None, None, None, 4, Hx, 64, 0, None) == -1

@@ -157,6 +157,33 @@ def test_long_prefill_full(G, T):
     assert (got.bank == inp.bank).all(), "bank (or its padding) modified"
 
 
+# The any-H kernel with three bank rows in LDS: 5-wave workgroups (H 4104..5120),
+# 4..8 bank rows, more tokens than three per compute unit (T > 768 on 256 CUs);
+# masked rows, and the cached-read form (T * H >= 1024 * 7168 with a delta and
+# a written source slot).
+LDS_ROW_CASES = [
+    dict(H=5120, T=1024, nb=8, widx=3),
+    dict(H=5120, T=1000, nb=4, has_onorm=False, widx=-1),
+    dict(H=5120, T=900, nb=6, has_delta=False, widx=5),
+    dict(H=4608, T=1100, nb=7, widx=0),                          # masked
+    dict(H=4104, T=800, nb=5, has_delta=False, has_onorm=False),  # masked, one segment over
+    dict(H=5120, T=1500, nb=8, widx=2, token_pad=64),            # cached rewritten rows
+    dict(H=4616, T=1700, nb=5, widx=4, recipe="soft"),           # masked and cached
+]
+
+
+@pytest.mark.parametrize("kw", LDS_ROW_CASES, ids=lambda kw: "_".join(f"{k}{v}" for k, v in kw.items()))
+def test_any_h_rows_in_lds(G, kw):
+    case = W.Case("lds_rows_" + "_".join(f"{k}{v}" for k, v in kw.items()), seed=77, **kw)
+    inp = W.make_inputs(case)
+    ref = G.oracle_full_threaded(inp)
+    for path in (None, A_PATH_ANY_H):
+        G.say(case.name, "path", path)
+        d = G.upload(inp)
+        G.run(d, path=path)
+        G.check_full(inp, G.download(d), ref)
+
+
 @pytest.mark.parametrize("case", W.variant_matrix(), ids=lambda c: c.name)
 def test_variant_matrix(G, case):
     inp = W.make_inputs(case)
