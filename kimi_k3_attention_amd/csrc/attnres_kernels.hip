@@ -1833,25 +1833,6 @@ int compute_units(int dev, int *cus) {
 
 // noalloc: the split path takes the static scratch instead of the allocated
 // workspace, and no stream hand-off is made (calls that overlap race).
-// Lets a kernel of the LDS-row variant take its dynamic LDS beyond the
-// default limit, once per kernel.  Where the runtime has no such limit the
-// attribute may be refused; the launch's own status then decides.
-std::mutex g_lds_attr_mu;
-const void *g_lds_attr_done[256];
-void allow_dynamic_lds(KernelFn fn, size_t bytes) {
-  const void *f = reinterpret_cast<const void *>(fn);
-  std::lock_guard<std::mutex> lock(g_lds_attr_mu);
-  for (const void *d : g_lds_attr_done)
-    if (d == f) return;
-  if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes)) != hipSuccess)
-    (void)hipGetLastError();
-  for (const void *&d : g_lds_attr_done)
-    if (d == nullptr) {
-      d = f;
-      break;
-    }
-}
-
 int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
   if (path != ATTNRES_PATH_AUTO && path != ATTNRES_PATH_ROW && path != ATTNRES_PATH_SPLIT &&
       path != ATTNRES_PATH_ANY_H)
@@ -1958,9 +1939,8 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
     size_t dyn = 0;
     KernelFn fn = nullptr;
     if (anyh_lds_rows(sh, a.T, a.num_blocks, cus, &dyn)) {
+      // at most 30 KB of dynamic LDS (320 lanes), under the default limit
       fn = pick_anyh_lds(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
-      // the largest LDS this kernel takes: at the most lanes of its shape
-      if (fn) allow_dynamic_lds(fn, size_t(kAnyLdsRows) * sh.spl * 384 * 16);
     }
     if (!fn) {
       dyn = 0;
