@@ -55,3 +55,15 @@ def test_row_kernel_fits_two_workgroups_per_cu(tmp_path):
     row = {n: k for n, k in ks.items() if "attnres_row_kernel" in n}
     assert len(row) == 9 * 4 + 8 * 4  # nb 0..8 x (delta, norm); cached variants at nb >= 1
     assert all(k["vgprs"] <= 128 for k in row.values()), row
+
+
+def test_any_h_lds_row_variant_fits_four_workgroups_per_cu(tmp_path):
+    """The any-H kernel with three bank rows in LDS exists to let four 5-wave
+    workgroups share a compute unit, which needs at most 96 VGPRs (five waves
+    per SIMD).  Only two segments per lane are built that way."""
+    ks = _kernels(tmp_path)
+    lds = {n: k for n, k in ks.items()
+           if "attnres_anyh_kernel" in n and n.endswith("Li3EEEvNS0_7KParamsE")}
+    assert len(lds) == 2 * 5 * 8  # masked or not x nb 4..8 x (delta, norm, cached)
+    assert all("ILi2E" in n for n in lds), "LDS rows are built for two segments per lane only"
+    assert all(k["vgprs"] <= 96 for k in lds.values()), lds
