@@ -76,9 +76,12 @@
 #ifndef ATTNRES_SPLIT_MFMA_WORDS
 #define ATTNRES_SPLIT_MFMA_WORDS 40     // split path: from this many words, one matrix-core product
 #endif
-#ifndef ATTNRES_EARLY_CUR_STORE
-#define ATTNRES_EARLY_CUR_STORE 0       // write prefix / bank rows as soon as cur exists
+#ifndef ATTNRES_CUR_FIRST
+#define ATTNRES_CUR_FIRST 1             // issue prefix and delta before the bank rows
 #endif
+#ifndef ATTNRES_EARLY_CUR_STORE
+#define ATTNRES_EARLY_CUR_STORE 1       // row kernel, cached in-place rows: write prefix /
+#endif                                  // bank rows once every load has landed, not with out
 
 namespace attnres {
 namespace {
@@ -319,6 +322,31 @@ struct Token {
     return ok ? load_cached(q) : zero;
   }
 
+  // prefix and delta (cur's rows) before the bank rows, from three bank rows
+  // up: cur's arithmetic, the longest of any source's (the add and rounding,
+  // then its partials), then overlaps the bank rows' arrival instead of
+  // following the last load.  With one or two bank rows the other order
+  // measured faster.  (The LDS-row variant keeps its own order.)
+  static constexpr bool kCurFirst = ATTNRES_CUR_FIRST && CUR && LR == 0 && NB >= 3;
+
+  // cur's rows: prefix (through the cache when the call rewrites it) and delta.
+  __device__ __forceinline__ void issue_cur(const KParams &p, int64_t t, const uint16_t *prow,
+                                            const uint32_t (&sb)[SPL], const bool (&ok)[SPL]) {
+    if constexpr (CUR) {
+      if constexpr (CACHE_RW && DELTA) {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) x[NB][i] = load_rewritten(p, prow, sb[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(at(prow, sb[i]), ok[i]);
+      }
+      if constexpr (DELTA)
+#pragma unroll
+        for (int i = 0; i < SPL; ++i)
+          d[i] = load_row(at(p.delta + t * p.delta_stride, sb[i]), ok[i]);
+    }
+  }
+
   __device__ __forceinline__ void issue(const KParams &p, int64_t t, int seg0, int seg_step) {
     bool ok[SPL];
     uint32_t sb[SPL];
@@ -336,6 +364,10 @@ struct Token {
       }
     const uint16_t *bank = p.blocks + t * p.tok_stride;
     const uint16_t *prow = p.prefix + t * p.prefix_stride;
+    if constexpr (kCurFirst) {
+      issue_cur(p, t, prow, sb, ok);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (!CUR) {
       // The bank rows alone, in source order.
 #pragma unroll
@@ -370,13 +402,6 @@ struct Token {
         for (int i = 0; i < SPL; ++i) x[NB - 1][i] = load_rewritten(p, row, sb[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (DELTA) {
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) x[NB][i] = load_rewritten(p, prow, sb[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(at(prow, sb[i]), ok[i]);
-      }
     } else {
       // Rows are issued in source order (the scheduler would otherwise order
       // them by when their addresses are ready), so that the partials of each
@@ -388,13 +413,8 @@ struct Token {
           x[j][i] = load_row(at(bank + j * p.slot_stride, sb[i]), ok[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(at(prow, sb[i]), ok[i]);
     }
-    if constexpr (DELTA)
-#pragma unroll
-      for (int i = 0; i < SPL; ++i)
-        d[i] = load_row(at(p.delta + t * p.delta_stride, sb[i]), ok[i]);
+    if constexpr (!kCurFirst) issue_cur(p, t, prow, sb, ok);
     if constexpr (LR > 0) {
       // The first LR sources last, straight into LDS: in the cached variant
       // the first LR of the ascending slots other than widx, else slots
@@ -428,6 +448,25 @@ struct Token {
       for (int i = 0; i < SPL; ++i) {
         onw[i] = load_weight(at(p.onw, seg_bytes(seg0, seg_step, i)), in_row(p, seg0 + i * seg_step));
       }
+  }
+
+  // Between the last source's partials and the logits (row and any-H
+  // kernels): the workgroup barrier, then the output-norm weight's load; or,
+  // EARLY, that load, then cur's in-place writes (every load of the lane has
+  // landed), then the barrier.  The weight goes first because loads and
+  // stores share one in-order counter: a load issued after the writes would
+  // wait for them.
+  template <bool EARLY>
+  __device__ __forceinline__ void after_partials(const KParams &p, int64_t t, int seg0,
+                                                 int seg_step) {
+    if constexpr (EARLY) {
+      issue_onw(p, seg0, seg_step);
+      store_cur(p, t, seg0, seg_step);
+      __syncthreads();
+    } else {
+      __syncthreads();
+      issue_onw(p, seg0, seg_step);
+    }
   }
 
   // Fused query q = rms_w * res_w, split exactly into two packed bf16 words:
@@ -559,11 +598,10 @@ struct Token {
       }
   }
 
-  // The in-place writes of cur (prefix with a delta, bank slot widx).  By the
-  // time cur exists every load of this lane has completed (the wait counter
-  // retires loads in issue order and prefix / delta were issued last), and a
-  // lane only rewrites elements it has already read, so the writes may be
-  // issued from then on.
+  // The in-place writes of cur (prefix with a delta, bank slot widx).  A lane
+  // only rewrites elements it has read itself; the writes go out once all of
+  // its loads have completed: with out, or right after the last source's
+  // partials, whose wait retires every earlier load (after_partials).
   __device__ __forceinline__ void store_cur(const KParams &p, int64_t t, int seg0,
                                             int seg_step) const {
 #pragma unroll
@@ -578,14 +616,15 @@ struct Token {
     }
   }
 
-  // The in-place writes of cur (unless already done), then out =
+  // The in-place writes of cur (unless CUR_DONE: already issued), then out =
   // bf16_RNE(y * rsig * w) (or y).  Writing cur first was faster everywhere
   // measured (T = 1, nb = 0: 2.70 -> 2.65 us; T = 1024, nb = 8: 32.76 ->
   // 32.63 us; T = 512-768: about 2 %): the rewritten lines are still
   // resident when those rows were read through the cache.
+  template <bool CUR_DONE = false>
   __device__ __forceinline__ void store(const KParams &p, int64_t t, int seg0, int seg_step,
                                         const float (&y)[SPL][8], float rsig) const {
-    if (!ATTNRES_EARLY_CUR_STORE) store_cur(p, t, seg0, seg_step);
+    if constexpr (!CUR_DONE) store_cur(p, t, seg0, seg_step);
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
       if (!in_row(p, seg0 + i * seg_step)) continue;
@@ -713,6 +752,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kRowThreads, kRowThre
 attnres_row_kernel(KParams p) {
   constexpr int NS = NB + 1;
   constexpr int SPL = kRowSegsPerLane;
+  // cur's in-place writes as soon as every load has landed, in the variant
+  // that read those rows through the cache (calls of T * H >= 1024 * 7168):
+  // there T = 1024 with 4 or 8 bank rows measured 1.2-1.8 % faster, T =
+  // 2048-4096 within 0.4 %.  Smaller calls, whose rows stream past the cache,
+  // measured slower (T = 256 +6 %), and so did the any-H kernel's forms.
+  constexpr bool kEarlyCur = ATTNRES_EARLY_CUR_STORE && CACHE_RW;
   __shared__ __align__(16) float s_part[2][2 * NS][kRowRows];
   __shared__ __align__(16) float s_ysq[2][kRowRows];
 
@@ -757,15 +802,13 @@ attnres_row_kernel(KParams p) {
     tk.query(qh, ql);
 
     // Each source's partials as soon as its rows land (loads retire in issue
-    // order: the bank rows, then prefix and delta), reduced within 16-lane
-    // rows and parked in LDS, so that this work overlaps the later rows'
-    // arrival; cur (prefix + delta, issued last) comes last.
+    // order), reduced within 16-lane rows and parked in LDS, so that this
+    // work overlaps the later rows' arrival.  cur (prefix + delta) comes in
+    // the order its rows were issued: first by default.
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      if (j == NB) {
-        tk.finish_cur();
-        if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, seg0, seg_step);
-      }
+    for (int jj = 0; jj < NS; ++jj) {
+      const int j = decltype(tk)::kCurFirst ? (jj == 0 ? NB : jj - 1) : jj;
+      if (j == NB) tk.finish_cur();
       float sj, dj;
       tk.partial(j, qh, ql, sj, dj);
       sj = row16_sum(sj);
@@ -777,8 +820,7 @@ attnres_row_kernel(KParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     tk.keep_packed();
-    __syncthreads();
-    tk.issue_onw(p, seg0, seg_step);
+    tk.template after_partials<kEarlyCur>(p, t, seg0, seg_step);
 
     // Lane j < NS sums source j's squares and lane 32 + j its query dots;
     // lane j then takes the dot from lane 32 + j.
@@ -798,7 +840,7 @@ attnres_row_kernel(KParams p) {
       __syncthreads();
       rsig = rsqrtf(wave_sum_of_partials(s_ysq[par], kRowRows) * kInvHidden + p.out_eps);
     }
-    tk.store(p, t, seg0, seg_step, y, rsig);
+    tk.template store<kEarlyCur>(p, t, seg0, seg_step, y, rsig);
   }
 }
 
@@ -892,12 +934,13 @@ attnres_anyh_kernel(KParams p) {
   u32x4 qh[SPL], ql[SPL];
   tk.query(qh, ql);
 
-  // Each source's partials as its rows land, cur last (as in the row kernel);
-  // then the LDS rows, issued last, once every load has landed.
+  // Each source's partials as its rows land, in issue order as in the row
+  // kernel; then the LDS rows, issued last, once every load has landed.
 #pragma unroll
   for (int j = LR; j < NS + LR; ++j) {
-    const int src = j < NS ? j : j - NS;
-    if (j == NB) tk.finish_cur();
+    const int src0 = j < NS ? j : j - NS;
+    const int src = decltype(tk)::kCurFirst ? (j == 0 ? NB : j - 1) : src0;
+    if (src == NB) tk.finish_cur();
     if (j == NS) tk.wait_lds_rows();
     float sj, dj;
     tk.partial(src, qh, ql, sj, dj);
@@ -910,8 +953,7 @@ attnres_anyh_kernel(KParams p) {
     __builtin_amdgcn_sched_barrier(0);
   }
   tk.keep_packed();
-  __syncthreads();
-  tk.issue_onw(p, seg0, seg_step);
+  tk.template after_partials<false>(p, t, seg0, seg_step);
 
   // Lane j < NS sums source j's squares, lane 32 + j its query dots.
   float tot = 0.f;
@@ -1291,7 +1333,6 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   u32x4 qh[SPL], ql[SPL];
   tk.query(qh, ql);
   tk.finish_cur();
-  if (ATTNRES_EARLY_CUR_STORE) tk.store_cur(p, t, seg0, seg_step);
 
   // Per-lane values summed over the wave, then published with one store of
   // tagged words (lane v holds word v).  A few words are summed with DPP

@@ -70,6 +70,21 @@ def test_traffic_is_scaled_by_the_calibration_copy(tmp_path, profiles_dir):
     assert "# command: cmd" in stats and "33.600" in stats
 
 
+def test_source_hash_ignores_comments_and_layout_only():
+    src = (b'#define N 4  // rows\n'
+           b'__device__ int f(int x) { /* twice */ return x * 2; }\n'
+           b'const char *s = "a // b"; char c = \'"\';\n')
+    same = (b'// a note\n#define N 4\n\n'
+            b'__device__   int f(int x)   {  return x * 2; } // done\n'
+            b'const char *s = "a // b";   char c = \'"\';\n')
+    assert bench.code_only(src) == bench.code_only(same)
+    # code, string contents and line structure still count
+    for other in (src.replace(b"x * 2", b"x * 3"), src.replace(b'"a // b"', b'"a b"'),
+                  src.replace(b"4  // rows\n", b"4 ")):
+        assert bench.code_only(other) != bench.code_only(src)
+    assert bench.code_only(b"int a; /* unterminated") == b"int a;"
+
+
 def test_stale_traffic_is_not_reported(profiles_dir):
     os.makedirs(profiles_dir)
     with open(bench.TRAFFIC_FILE, "w") as f:
