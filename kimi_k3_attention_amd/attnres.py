@@ -168,6 +168,20 @@ def _dense(m) -> bool:
     return m["ps"] == m["H"] and m["ds"] == m["H"] and m["os"] == m["H"]
 
 
+def _device_of(prefix: torch.Tensor, **others: Optional[torch.Tensor]) -> torch.device:
+    """prefix's GPU, once every other tensor argument is on it too: the kernels
+    dereference every pointer on that device, so a host tensor or one on
+    another GPU would fault there and is refused here."""
+    dev = prefix.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for name, t in others.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, prefix on {dev}: all tensors must be "
+                             "on the same GPU")
+    return dev
+
+
 def attnres_fwd(prefix: torch.Tensor, delta: Optional[torch.Tensor],
                 blocks: Optional[torch.Tensor], num_blocks: int, res_w: torch.Tensor,
                 rms_w: torch.Tensor, rms_eps: float,
@@ -184,16 +198,8 @@ def attnres_fwd(prefix: torch.Tensor, delta: Optional[torch.Tensor],
     """
     m = _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
                  output_norm_eps, block_write_idx, out)
-    dev = prefix.device
-    if dev.type != "cuda":
-        raise ValueError("tensors must be on a GPU")
-    # The kernels dereference every pointer on prefix's device: a host tensor
-    # or one on another GPU would fault there, so it is refused here.
-    for name, t in (("delta", delta), ("blocks", blocks), ("res_w", res_w), ("rms_w", rms_w),
-                    ("output_norm_weight", output_norm_weight), ("out", out)):
-        if t is not None and t.device != dev:
-            raise ValueError(f"{name} is on {t.device}, prefix on {dev}: all tensors must be "
-                             "on the same GPU")
+    dev = _device_of(prefix, delta=delta, blocks=blocks, res_w=res_w, rms_w=rms_w,
+                     output_norm_weight=output_norm_weight, out=out)
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         if not _dense(m):
@@ -222,14 +228,8 @@ def attnres_fwd_noalloc(prefix: torch.Tensor, delta: Optional[torch.Tensor],
     that overlap on one GPU race).  Same arguments as attnres_fwd."""
     m = _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
                  output_norm_eps, block_write_idx, out)
-    dev = prefix.device
-    if dev.type != "cuda":
-        raise ValueError("tensors must be on a GPU")
-    for name, t in (("delta", delta), ("blocks", blocks), ("res_w", res_w), ("rms_w", rms_w),
-                    ("output_norm_weight", output_norm_weight), ("out", out)):
-        if t is not None and t.device != dev:
-            raise ValueError(f"{name} is on {t.device}, prefix on {dev}: all tensors must be "
-                             "on the same GPU")
+    dev = _device_of(prefix, delta=delta, blocks=blocks, res_w=res_w, rms_w=rms_w,
+                     output_norm_weight=output_norm_weight, out=out)
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         rc = _lib.attnres_fwd_noalloc(*_strided_args(m), s.cuda_stream,
@@ -250,15 +250,8 @@ def _two_part(fn_name, prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps,
               output_norm_weight, output_norm_eps, block_write_idx, out, partial, stream):
     m = _marshal(prefix, delta, blocks, num_blocks, res_w, rms_w, rms_eps, output_norm_weight,
                  output_norm_eps, block_write_idx, out)
-    dev = prefix.device
-    if dev.type != "cuda":
-        raise ValueError("tensors must be on a GPU")
-    for name, t in (("delta", delta), ("blocks", blocks), ("res_w", res_w), ("rms_w", rms_w),
-                    ("output_norm_weight", output_norm_weight), ("out", out),
-                    ("partial", partial)):
-        if t is not None and t.device != dev:
-            raise ValueError(f"{name} is on {t.device}, prefix on {dev}: all tensors must be "
-                             "on the same GPU")
+    dev = _device_of(prefix, delta=delta, blocks=blocks, res_w=res_w, rms_w=rms_w,
+                     output_norm_weight=output_norm_weight, out=out, partial=partial)
     nbytes = 0 if partial is None else partial.numel() * partial.element_size()
     if partial is not None and not partial.is_contiguous():
         raise ValueError("partial must be contiguous")

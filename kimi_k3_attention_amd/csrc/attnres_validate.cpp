@@ -198,7 +198,7 @@ const char *strerror_text(int status) {
     case ATTNRES_OK: return "ok";
     case ATTNRES_E_NULL: return "a required pointer is NULL";
     case ATTNRES_E_SHAPE: return "invalid or too large T, H, max_blocks or stride";
-    case ATTNRES_E_UNSUPPORTED: return "unsupported size (H must be a multiple of 8 up to 16384; the split path needs H = 7168 and T <= 256)";
+    case ATTNRES_E_UNSUPPORTED: return "unsupported size (H must be a multiple of 8 up to 16384; the split path takes T <= 256)";
     case ATTNRES_E_NUM_BLOCKS: return "num_blocks must be in 0..min(8, max_blocks)";
     case ATTNRES_E_WRITE_IDX: return "block_write_idx must be -1 or in 0..max_blocks-1";
     case ATTNRES_E_ALIGN: return "pointers must be 16-byte aligned and strides multiples of 8 elements";
