@@ -243,6 +243,78 @@ def test_row_overlap_check_against_brute_force(A):
     assert checked_equal > 500
 
 
+def test_accepted_layouts_never_share_a_written_element(A):
+    """Every buffer at once, on the host: prefix, delta, a bank with random
+    token and slot strides (token- or slot-major, padded or interleaved),
+    out and the three weights, placed at random 16-byte offsets in a small
+    address range so that they often meet.  Whenever the library accepts a
+    layout, no element the call writes (out; prefix with a delta; bank slot
+    block_write_idx of every token) is shared with any other element the
+    call reads or writes, and distinct bank rows, prefix rows and out rows
+    are disjoint.  Element sets are enumerated exactly."""
+    rng = np.random.default_rng(23)
+    h = 16
+    accepted = rejected = 0
+    for _ in range(4000):
+        T = int(rng.integers(1, 5))
+        cap = int(rng.integers(1, 4))
+        nb = int(rng.integers(0, cap + 1))
+        widx = int(rng.integers(-1, cap))
+        has_d, has_o = rng.random() < 0.7, rng.random() < 0.7
+        ps = h + 8 * int(rng.integers(0, 5))
+        ds = h + 8 * int(rng.integers(0, 5))
+        os_ = h + 8 * int(rng.integers(0, 5))
+        if rng.random() < 0.5:                       # token-major, maybe padded
+            ss = h + 8 * int(rng.integers(0, 3))
+            ts = cap * ss + 8 * int(rng.integers(-2, 4))
+        else:                                        # slot-major
+            ts = h + 8 * int(rng.integers(0, 3))
+            ss = T * ts + 8 * int(rng.integers(-2, 4))
+        ts, ss = max(ts, 0), max(ss, 0)
+
+        def place():
+            return 0x1000000 + 16 * int(rng.integers(0, 64))
+
+        a = dict(prefix=place(), ps=ps, delta=place() if has_d else None, ds=ds,
+                 blocks=place(), ts=ts, ss=ss, cap=cap, nb=nb, res_w=place(), rms_w=place(),
+                 eps=1e-6, onw=place() if has_o else None, oeps=1e-6, widx=widx, out=place(),
+                 os=os_, T=T, H=h)
+        rc = _validate_strided(A, a)
+        if rc != 0:
+            assert A.STATUS[rc] in ("ATTNRES_E_ALIAS", "ATTNRES_E_STRIDE"), A.STATUS[rc]
+            rejected += 1
+            continue
+        accepted += 1
+
+        def row(base, off):
+            return {base + 2 * (off + k) for k in range(h)}
+
+        bank_used = nb > 0 or widx >= 0
+        reads, writes = [], []                       # (label, element set)
+        for t in range(T):
+            reads.append((("prefix", t), row(a["prefix"], t * ps)))
+            if has_d:
+                reads.append((("delta", t), row(a["delta"], t * ds)))
+                writes.append((("prefix", t), row(a["prefix"], t * ps)))
+            writes.append((("out", t), row(a["out"], t * os_)))
+            if bank_used:
+                for i in range(cap):
+                    reads.append((("bank", t, i), row(a["blocks"], t * ts + i * ss)))
+                if widx >= 0:
+                    writes.append((("bank", t, widx), row(a["blocks"], t * ts + widx * ss)))
+        for name in ("res_w", "rms_w", "onw"):
+            if a[name] is not None:
+                reads.append(((name,), row(a[name], 0)))
+        everything = reads + [w for w in writes if w[0][0] == "out"]
+        for wl, we in writes:
+            for ol, oe in everything:
+                if ol != wl:
+                    assert not (we & oe), (a, wl, ol)
+        banks = [e for l, e in reads if l[0] == "bank"]
+        assert sum(len(e) for e in banks) == len(set().union(*banks)) if banks else True, a
+    assert accepted > 300 and rejected > 300, (accepted, rejected)
+
+
 def test_read_only_overlaps_are_allowed(A):
     # prefix read-only (no delta) may share memory with a read-only bank and
     # with the weights; only written buffers must be exclusive.
