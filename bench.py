@@ -418,7 +418,7 @@ def _host_threads() -> int:
     return max(1, min(16, n))
 
 
-HIDDEN_SWEEP = (2048, 2880, 4096, 5120, 7168, 8192, 12288, 16384)
+HIDDEN_SWEEP = (2048, 2880, 4096, 5120, 7168, 8192, 9216, 11264, 12288, 16384)
 
 
 def anyh_threads(H: int) -> int:

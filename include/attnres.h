@@ -272,8 +272,10 @@ int attnres_validate_strided(const void *prefix, int64_t prefix_stride,
 
 /* Allocates and clears the split path's workspace on `device` (about 1.8 MB:
  * tagged partial-sum words and a fault flag), and takes the address of (and
- * clears) attnres_fwd_noalloc's static array there.  Idempotent.
- * Call it outside stream capture. */
+ * clears) attnres_fwd_noalloc's static array there.  It also lets the any-H
+ * kernels that stage bank rows in LDS (H = 8200..12288) take their 61-72 KB of
+ * dynamic LDS, which a call would otherwise set up at its first use.
+ * Idempotent.  Call it outside stream capture. */
 int attnres_init(int device);
 
 /* Frees every device's workspace.  No call may be in flight. */

@@ -76,6 +76,9 @@
 #ifndef ATTNRES_SPLIT_MFMA_WORDS
 #define ATTNRES_SPLIT_MFMA_WORDS 40     // split path: from this many words, one matrix-core product
 #endif
+#ifndef ATTNRES_ANYH_STAGED
+#define ATTNRES_ANYH_STAGED 1           // any-H, four segments: three bank rows staged in LDS
+#endif
 #ifndef ATTNRES_CUR_FIRST
 #define ATTNRES_CUR_FIRST 1             // issue prefix and delta before the bank rows
 #endif
@@ -105,6 +108,7 @@ constexpr int kSlotYsq = kSlot - 1;           // where a part's sum of y^2 goes
 constexpr int kSpinLimit = 1 << 20;           // bounded cross-workgroup wait
 // Fourth word of a raw buffer resource: 32-bit data format, no swizzle.
 constexpr int kBufferFormat = 0x00020000;
+constexpr int kAuxNt = 2;  // cache-policy operand of a load: non-temporal
 constexpr float kInvHidden = 1.0f / kHidden;
 
 // Row path grid.  With few source rows a token moves little data, and with
@@ -249,11 +253,22 @@ __device__ __forceinline__ float lane_shuffle(float v, int src) {
 // (global_load_lds, 16 bytes per lane, no registers), issued after every
 // other row; they are read back from LDS when used.  That frees 4 SPL
 // registers per row, so more workgroups fit a CU (see the any-H kernel).
+// STG (with LR > 0): the LR rows are staged instead.  They are loaded into
+// registers right after cur's rows, their partials are taken as they land,
+// and then each lane copies them to LDS.  Only then are the last bank rows
+// issued (issue_rest), into the registers the staged rows held.  Every load
+// is a plain one, so the waits stay progressive; with LDS-direct loads in
+// flight the compiler waits for all loads at the first use of any.
 template <int NB, bool DELTA, bool ONORM, int SPL, bool MASKED = false, bool CACHE_RW = false,
-          bool CUR = true, bool Q = (NB > 0), int LR = 0>
+          bool CUR = true, bool Q = (NB > 0), int LR = 0, bool STG = false>
 struct Token {
   static constexpr int NS = NB + (CUR ? 1 : 0);
   static_assert(LR == 0 || (CUR && LR < NB), "LDS rows are bank rows of a full token");
+  static_assert(!STG || LR > 0, "staging needs LDS rows");
+  // STG: bank rows (in issue order) of the first burst, the staged ones;
+  // the rest follow the staging.  With cur's two rows and the weights that
+  // is what four segments per lane leave room for at 168 VGPRs.
+  static constexpr int kFirst = STG ? LR : NB;
   u32x4 rms[SPL], res[SPL], onw[SPL];  // weights
   u32x4 x[NB + 1][SPL];                // bank slots 0..NB-1, then prefix (cur after finish_cur)
   u32x4 d[SPL];                        // delta
@@ -262,19 +277,27 @@ struct Token {
   bool seg_ok[SPL];
 
   // Source j, segment i: from LDS for the first LR sources (zero past a
-  // masked row's end), else from registers.
+  // masked row's end: staged rows carry the zeros their loads gave), else
+  // from registers.
   __device__ __forceinline__ u32x4 row(int j, int i) const {
     if (j < LR) {
       const u32x4 zero = {0u, 0u, 0u, 0u};
       const u32x4 v = lds_rows[(j * SPL + i) * nthr + int(threadIdx.x)];
-      return MASKED && !seg_ok[i] ? zero : v;
+      return MASKED && !STG && !seg_ok[i] ? zero : v;
     }
     return x[j][i];
   }
   // The LDS rows are written by the memory system behind the compiler's
-  // back: wait for every load in flight before reading them.
+  // back: wait for every load in flight before reading them.  (Staged rows
+  // are written by the lanes themselves, which the compiler tracks.)
   __device__ __forceinline__ static void wait_lds_rows() {
-    if constexpr (LR > 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if constexpr (LR > 0 && !STG) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
+  // STG: staged row k from this lane's registers to its own LDS slots.
+  __device__ __forceinline__ void stage(int k) {
+    if constexpr (STG)
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) lds_rows[(k * SPL + i) * nthr + int(threadIdx.x)] = x[k][i];
   }
 
   __device__ __forceinline__ static bool in_row(const KParams &p, int seg) {
@@ -285,10 +308,20 @@ struct Token {
   // would then form a 64-bit address for every row (and keep the stores'
   // live through the kernel); held opaque in one 32-bit register, it is
   // shared by all rows, each addressed as scalar row base + this offset.
+  // STG: recomputed at every use, from a fresh opaque copy of seg0 (kept
+  // live anyway), so that the offsets are not merged into values live
+  // through the kernel: there they spilled, and a spill's reload waits for
+  // every load and store in flight.
   __device__ __forceinline__ static uint32_t seg_bytes(int seg0, int seg_step, int i) {
-    uint32_t b = uint32_t(seg0 + i * seg_step) * uint32_t(kSeg * sizeof(uint16_t));
-    if (i > 0) asm("" : "+v"(b));
-    return b;
+    if constexpr (STG) {
+      uint32_t s0 = uint32_t(seg0);
+      if (i > 0) asm volatile("" : "+v"(s0));
+      return (s0 + uint32_t(i * seg_step)) * uint32_t(kSeg * sizeof(uint16_t));
+    } else {
+      uint32_t b = uint32_t(seg0 + i * seg_step) * uint32_t(kSeg * sizeof(uint16_t));
+      if (i > 0) asm("" : "+v"(b));
+      return b;
+    }
   }
   __device__ __forceinline__ static const uint16_t *at(const uint16_t *row, uint32_t b) {
     return reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(row) + b);
@@ -296,10 +329,23 @@ struct Token {
   __device__ __forceinline__ static uint16_t *at(uint16_t *row, uint32_t b) {
     return reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(row) + b);
   }
-  __device__ __forceinline__ static u32x4 load_row(const uint16_t *q, bool ok) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if (!MASKED) return load_stream(q);
-    return ok ? load_stream(q) : zero;
+  // A row's segment at byte offset b.  MASKED: a buffer load whose record is
+  // the row, so a segment at or past the row's end reads zero by the
+  // hardware's range check, with no branch: a branch around each load left
+  // the compiler unable to count the loads in flight, and every source's
+  // arithmetic then waited for all of them.
+  template <int AUX>
+  __device__ __forceinline__ static u32x4 load_in_row(const KParams &p, const uint16_t *row,
+                                                      uint32_t b) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(row), 0, p.nseg * kSeg * int(sizeof(uint16_t)), kBufferFormat);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(b), 0, AUX);
+  }
+  __device__ __forceinline__ static u32x4 load_row(const KParams &p, const uint16_t *row,
+                                                   uint32_t b, bool ok) {
+    (void)ok;
+    if constexpr (MASKED) return load_in_row<ATTNRES_NT_LOADS ? kAuxNt : 0>(p, row, b);
+    return load_stream(at(row, b));
   }
   // With CACHE_RW, the rows a call also writes (the bank slot widx, a source
   // here, and prefix when a delta is given) are read through the cache at
@@ -316,10 +362,11 @@ struct Token {
         const_cast<uint16_t *>(row), 0, p.nseg * kSeg * int(sizeof(uint16_t)), kBufferFormat);
     return __builtin_amdgcn_raw_buffer_load_b128(r, int(bytes), 0, 0);
   }
-  __device__ __forceinline__ static u32x4 load_weight(const uint16_t *q, bool ok) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if (!MASKED) return load_cached(q);
-    return ok ? load_cached(q) : zero;
+  __device__ __forceinline__ static u32x4 load_weight(const KParams &p, const uint16_t *w,
+                                                      uint32_t b, bool ok) {
+    (void)ok;
+    if constexpr (MASKED) return load_in_row<0>(p, w, b);
+    return load_cached(at(w, b));
   }
 
   // prefix and delta (cur's rows) before the bank rows, from three bank rows
@@ -327,7 +374,50 @@ struct Token {
   // then its partials), then overlaps the bank rows' arrival instead of
   // following the last load.  With one or two bank rows the other order
   // measured faster.  (The LDS-row variant keeps its own order.)
-  static constexpr bool kCurFirst = ATTNRES_CUR_FIRST && CUR && LR == 0 && NB >= 3;
+  static constexpr bool kCurFirst = STG || (ATTNRES_CUR_FIRST && CUR && LR == 0 && NB >= 3);
+
+  // Bank rows K0..K1-1 in issue order, each followed by a scheduling barrier.
+  // Issue order k is slot k, or in the cached variant the slots other than
+  // widx ascending and then widx (k = NB - 1) through the cache (see issue).
+  template <int K0, int K1>
+  __device__ __forceinline__ void issue_bank(const KParams &p, const uint16_t *bank,
+                                             const uint32_t (&sb)[SPL], const bool (&ok)[SPL]) {
+    constexpr int kPlain = CACHE_RW ? (K1 < NB - 1 ? K1 : NB - 1) : K1;
+#pragma unroll
+    for (int k = K0; k < kPlain; ++k) {
+      const int slot = CACHE_RW ? k + (k >= p.widx ? 1 : 0) : k;
+      const uint16_t *row = bank + slot * p.slot_stride;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) x[k][i] = load_row(p, row, sb[i], ok[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (CACHE_RW && K1 == NB) {
+      const uint16_t *row = bank + p.widx * p.slot_stride;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) x[NB - 1][i] = load_rewritten(p, row, sb[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // STG: bank rows K0..K1-1 of those after the first burst (clamped to NB),
+  // each as soon as registers are free for it: one once cur is formed
+  // (delta's registers), one after each staged row but the last, the rest
+  // after the last.
+  template <int K0, int K1>
+  __device__ __forceinline__ void issue_rest(const KParams &p, int64_t t, int seg0, int seg_step) {
+    constexpr int k0 = K0 < NB ? K0 : NB, k1 = K1 < NB ? K1 : NB;
+    if constexpr (STG && k0 < k1) {
+      bool ok[SPL];
+      uint32_t sb[SPL];
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        ok[i] = seg_ok[i];
+        sb[i] = seg_bytes(seg0, seg_step, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue_bank<k0, k1>(p, p.blocks + t * p.tok_stride, sb, ok);
+    }
+  }
 
   // cur's rows: prefix (through the cache when the call rewrites it) and delta.
   __device__ __forceinline__ void issue_cur(const KParams &p, int64_t t, const uint16_t *prow,
@@ -338,12 +428,12 @@ struct Token {
         for (int i = 0; i < SPL; ++i) x[NB][i] = load_rewritten(p, prow, sb[i]);
       } else {
 #pragma unroll
-        for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(at(prow, sb[i]), ok[i]);
+        for (int i = 0; i < SPL; ++i) x[NB][i] = load_row(p, prow, sb[i], ok[i]);
       }
       if constexpr (DELTA)
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-          d[i] = load_row(at(p.delta + t * p.delta_stride, sb[i]), ok[i]);
+          d[i] = load_row(p, p.delta + t * p.delta_stride, sb[i], ok[i]);
     }
   }
 
@@ -359,8 +449,8 @@ struct Token {
     if constexpr (Q)  // a single source needs no logit, hence no query
 #pragma unroll
       for (int i = 0; i < SPL; ++i) {
-        rms[i] = load_weight(at(p.rms_w, sb[i]), ok[i]);
-        res[i] = load_weight(at(p.res_w, sb[i]), ok[i]);
+        rms[i] = load_weight(p, p.rms_w, sb[i], ok[i]);
+        res[i] = load_weight(p, p.res_w, sb[i], ok[i]);
       }
     const uint16_t *bank = p.blocks + t * p.tok_stride;
     const uint16_t *prow = p.prefix + t * p.prefix_stride;
@@ -368,13 +458,19 @@ struct Token {
       issue_cur(p, t, prow, sb, ok);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (STG) {
+      // cur, then the staged rows and two more; the rest after the staging.
+      issue_bank<0, kFirst>(p, bank, sb, ok);
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     if constexpr (!CUR) {
       // The bank rows alone, in source order.
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-          x[j][i] = load_row(at(bank + j * p.slot_stride, sb[i]), ok[i]);
+          x[j][i] = load_row(p, bank + j * p.slot_stride, sb[i], ok[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -393,7 +489,7 @@ struct Token {
         const int slot = k + (k >= p.widx ? 1 : 0);
         const uint16_t *row = bank + slot * p.slot_stride;
 #pragma unroll
-        for (int i = 0; i < SPL; ++i) x[k][i] = load_row(at(row, sb[i]), ok[i]);
+        for (int i = 0; i < SPL; ++i) x[k][i] = load_row(p, row, sb[i], ok[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
       {
@@ -410,7 +506,7 @@ struct Token {
       for (int j = LR; j < NB; ++j) {
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-          x[j][i] = load_row(at(bank + j * p.slot_stride, sb[i]), ok[i]);
+          x[j][i] = load_row(p, bank + j * p.slot_stride, sb[i], ok[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -446,7 +542,7 @@ struct Token {
     if constexpr (ONORM)
 #pragma unroll
       for (int i = 0; i < SPL; ++i) {
-        onw[i] = load_weight(at(p.onw, seg_bytes(seg0, seg_step, i)), in_row(p, seg0 + i * seg_step));
+        onw[i] = load_weight(p, p.onw, seg_bytes(seg0, seg_step, i), in_row(p, seg0 + i * seg_step));
       }
   }
 
@@ -456,16 +552,18 @@ struct Token {
   // landed), then the barrier.  The weight goes first because loads and
   // stores share one in-order counter: a load issued after the writes would
   // wait for them.
-  template <bool EARLY>
+  // ONW = false: the weight is loaded later by the caller (after the
+  // mixture, where the rows no longer hold registers).
+  template <bool EARLY, bool ONW = true>
   __device__ __forceinline__ void after_partials(const KParams &p, int64_t t, int seg0,
                                                  int seg_step) {
     if constexpr (EARLY) {
-      issue_onw(p, seg0, seg_step);
+      if constexpr (ONW) issue_onw(p, seg0, seg_step);
       store_cur(p, t, seg0, seg_step);
       __syncthreads();
     } else {
       __syncthreads();
-      issue_onw(p, seg0, seg_step);
+      if constexpr (ONW) issue_onw(p, seg0, seg_step);
     }
   }
 
@@ -501,12 +599,14 @@ struct Token {
   }
 
   // Per-lane partial sum of squares and query dot of source j.
+  // REGS: from registers even for an LDS row (a staged row before staging).
+  template <bool REGS = false>
   __device__ __forceinline__ void partial(int j, const u32x4 (&qh)[SPL], const u32x4 (&ql)[SPL],
                                           float &ss, float &dq) const {
     float s = 0.f, dd = 0.f;
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
-      const u32x4 v = row(j, i);
+      const u32x4 v = REGS ? x[j][i] : row(j, i);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         s = dot2(v[k], v[k], s);
@@ -890,8 +990,10 @@ __device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
 // LR > 0 (kAnyLdsRows bank rows in LDS, launched with LR * SPL * blockDim.x
 // * 16 bytes of dynamic LDS): the same steps with those rows held in LDS
 // instead of registers, for one more resident workgroup per CU where the
-// registers are what limits it (see anyh_lds_rows).
-template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, int LR = 0>
+// registers are what limits it (see anyh_lds_rows).  STG: those rows reach
+// LDS through registers (staged; see Token), not by LDS-direct loads.
+template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, int LR = 0,
+          bool STG = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWave, kAnyMaxThreads),
                                amdgpu_waves_per_eu(LR == 0 ? (SPL <= 2 ? 4 : 2)
                                                            : (SPL <= 2 ? 5 : 3))))
@@ -911,7 +1013,7 @@ attnres_anyh_kernel(KParams p) {
   const int seg0 = int(threadIdx.x);  // whole-line loads, as in the row kernel
   const int seg_step = nthreads;
 
-  Token<NB, DELTA, ONORM, SPL, MASKED, CACHE_RW, true, (NB > 0), LR> tk;
+  Token<NB, DELTA, ONORM, SPL, MASKED, CACHE_RW, true, (NB > 0), LR, STG> tk;
   tk.lds_rows = s_rows;
   tk.nthr = p.threads;
   tk.issue(p, t, seg0, seg_step);
@@ -936,24 +1038,40 @@ attnres_anyh_kernel(KParams p) {
 
   // Each source's partials as its rows land, in issue order as in the row
   // kernel; then the LDS rows, issued last, once every load has landed.
+  // STG: cur, then bank rows in order; a staged row goes to LDS right after
+  // its partials, and each step releases the next loads (issue_rest).
 #pragma unroll
-  for (int j = LR; j < NS + LR; ++j) {
+  for (int j = STG ? 0 : LR; j < NS + (STG ? 0 : LR); ++j) {
     const int src0 = j < NS ? j : j - NS;
     const int src = decltype(tk)::kCurFirst ? (j == 0 ? NB : j - 1) : src0;
     if (src == NB) tk.finish_cur();
     if (j == NS) tk.wait_lds_rows();
     float sj, dj;
-    tk.partial(src, qh, ql, sj, dj);
+    if (STG && src < LR)
+      tk.template partial<true>(src, qh, ql, sj, dj);
+    else
+      tk.partial(src, qh, ql, sj, dj);
     sj = row16_sum(sj);
     dj = row16_sum(dj);
     if (row_leader) {
       s_part[src][rowslot] = sj;
       s_part[NS + src][rowslot] = dj;
     }
+    if constexpr (STG) {
+      static_assert(!STG || LR == 3, "the release points below are for three staged rows");
+      constexpr int F = decltype(tk)::kFirst;
+      if (src == NB) tk.template issue_rest<F, F + 1>(p, t, seg0, seg_step);
+      if (src < LR) tk.stage(src);
+      if (src == 0) tk.template issue_rest<F + 1, F + 2>(p, t, seg0, seg_step);
+      if (src == 1) tk.template issue_rest<F + 2, F + 3>(p, t, seg0, seg_step);
+      if (src == 2) tk.template issue_rest<F + 3, NB>(p, t, seg0, seg_step);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   tk.keep_packed();
-  tk.template after_partials<false>(p, t, seg0, seg_step);
+  // STG: the output-norm weight after the mixture (registers are tightest
+  // while the mixture runs), overlapping the norm's reduction.
+  tk.template after_partials<false, !STG>(p, t, seg0, seg_step);
 
   // Lane j < NS sums source j's squares, lane 32 + j its query dots.
   float tot = 0.f;
@@ -966,6 +1084,7 @@ attnres_anyh_kernel(KParams p) {
   float y[SPL][8];
   tk.keep_packed();
   tk.mix(p_lane, y);
+  if constexpr (STG) tk.issue_onw(p, seg0, seg_step);
 
   float rsig = 1.f;
   if constexpr (ONORM) {
@@ -1595,6 +1714,40 @@ KernelFn pick_anyh_lds(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw
   }
 }
 
+// The any-H kernel with kAnyLdsRows bank rows staged into LDS through
+// registers (four segments per lane, 4..8 bank rows).
+template <bool MASKED, int NB>
+KernelFn anyh_staged_fn(bool d, bool o, bool c) {
+  if constexpr (NB >= 4) {
+    constexpr int L = kAnyLdsRows;
+    if (c) {
+      if (d)
+        return o ? attnres_anyh_kernel<4, MASKED, NB, true, true, true, L, true>
+                 : attnres_anyh_kernel<4, MASKED, NB, true, false, true, L, true>;
+      return o ? attnres_anyh_kernel<4, MASKED, NB, false, true, true, L, true>
+               : attnres_anyh_kernel<4, MASKED, NB, false, false, true, L, true>;
+    }
+    if (d)
+      return o ? attnres_anyh_kernel<4, MASKED, NB, true, true, false, L, true>
+               : attnres_anyh_kernel<4, MASKED, NB, true, false, false, L, true>;
+    return o ? attnres_anyh_kernel<4, MASKED, NB, false, true, false, L, true>
+             : attnres_anyh_kernel<4, MASKED, NB, false, false, false, L, true>;
+  }
+  return nullptr;
+}
+KernelFn pick_anyh_staged(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw) {
+  if (sh.spl != 4) return nullptr;
+  switch (nb) {
+#define ATTNRES_CASE(N)                                              \
+  case N:                                                            \
+    return sh.masked ? anyh_staged_fn<true, N>(d, o, cache_rw)       \
+                     : anyh_staged_fn<false, N>(d, o, cache_rw);
+    ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
+#undef ATTNRES_CASE
+    default: return nullptr;
+  }
+}
+
 // Whether an any-H call holds kAnyLdsRows bank rows in LDS, and the dynamic
 // LDS bytes it then takes.  Registers bound the resident workgroups per CU of
 // the plain kernel: at two segments per lane it may take 128 VGPRs (four
@@ -1614,6 +1767,27 @@ KernelFn pick_anyh_lds(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw
 bool anyh_lds_rows(const AnyShape &sh, int64_t T, int nb, int cus, size_t *dyn) {
   const int waves = sh.threads / kWave;
   if (sh.spl != 2 || waves != 5 || nb < 4 || T <= int64_t(3) * cus) return false;
+  *dyn = size_t(kAnyLdsRows) * sh.spl * sh.threads * 16;
+  return true;
+}
+
+// Whether an any-H call stages kAnyLdsRows bank rows into LDS, and the
+// dynamic LDS bytes it then takes.  At four segments per lane a token of
+// 5-6 waves (H = 8200..12288) fills a CU's registers (200+ VGPRs), one
+// workgroup per CU.  Staging three rows brings it under 168 (three waves per
+// SIMD), so two fit, with 61-74 KB of LDS each.  The cost is a second round
+// of loads per token (the rows after the staged ones wait for registers).
+// Measured (delta, norm, 8 bank rows, µs per call, plain / staged): 5 waves,
+// H = 8704 T = 300 22.3 / 21.2, T = 1024 53.7 / 51.7, T = 2048 97.5 / 94.2;
+// H = 9216 T = 4096 without delta or norm 150.7 / 141.9; H = 10240 T = 300
+// 23.5 / 22.5, T = 2048 103.7 / 105.9.  6 waves, H = 12288: T = 300 26.0 /
+// 25.3, T = 1024 64.8 / 65.6, T = 2048 119.2 / 121.8 (H = 11264 and 12032
+// alike).  So 5-wave workgroups from one token per CU up, 6-wave ones only
+// up to two.
+bool anyh_staged_rows(const AnyShape &sh, int64_t T, int nb, int cus, size_t *dyn) {
+  const int waves = sh.threads / kWave;
+  if (sh.spl != 4 || nb < 4 || T <= int64_t(cus)) return false;
+  if (waves > 6 || (waves == 6 && T > int64_t(2) * cus)) return false;
   *dyn = size_t(kAnyLdsRows) * sh.spl * sh.threads * 16;
   return true;
 }
@@ -1872,6 +2046,41 @@ int compute_units(int dev, int *cus) {
   return ATTNRES_OK;
 }
 
+// Lets `fn` take `bytes` of dynamic LDS, beyond the runtime's default per
+// workgroup limit; set once per kernel (the attribute stays with it).
+std::mutex g_lds_attr_mu;
+const void *g_lds_attr_done[128];  // more than the staged kernels
+int allow_dynamic_lds(KernelFn fn, size_t bytes) {
+  const void *f = reinterpret_cast<const void *>(fn);
+  std::lock_guard<std::mutex> lock(g_lds_attr_mu);
+  for (const void *d : g_lds_attr_done)
+    if (d == f) return ATTNRES_OK;
+  const hipError_t e =
+      hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+  if (e != hipSuccess) return hip_fail(e);
+  for (const void *&d : g_lds_attr_done)
+    if (d == nullptr) {
+      d = f;
+      break;
+    }
+  return ATTNRES_OK;
+}
+
+// The dynamic-LDS attribute of every staged any-H kernel, so that a first
+// call under graph capture makes no attribute call.
+int allow_staged_lds() {
+  const AnyShape shapes[2] = {{4, 6 * kWave, false}, {4, 6 * kWave, true}};
+  for (const AnyShape &sh : shapes)
+    for (int nb = 4; nb <= kMaxBlocks; ++nb)
+      for (int f = 0; f < 8; ++f) {
+        const KernelFn fn = pick_anyh_staged(sh, nb, f & 1, f & 2, f & 4);
+        if (!fn) continue;
+        const int rc = allow_dynamic_lds(fn, size_t(kAnyLdsRows) * 4 * 384 * 16);
+        if (rc != ATTNRES_OK) return rc;
+      }
+  return ATTNRES_OK;
+}
+
 // noalloc: the split path takes the static scratch instead of the allocated
 // workspace, and no stream hand-off is made (calls that overlap race).
 int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
@@ -1982,6 +2191,13 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
     if (anyh_lds_rows(sh, a.T, a.num_blocks, cus, &dyn)) {
       // at most 30 KB of dynamic LDS (320 lanes), under the default limit
       fn = pick_anyh_lds(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
+    } else if (ATTNRES_ANYH_STAGED && anyh_staged_rows(sh, a.T, a.num_blocks, cus, &dyn)) {
+      fn = pick_anyh_staged(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
+      if (fn) {
+        // the largest such workgroup (384 lanes) takes 72 KB
+        rc = allow_dynamic_lds(fn, size_t(kAnyLdsRows) * 4 * 384 * 16);
+        if (rc != ATTNRES_OK) return rc;
+      }
     }
     if (!fn) {
       dyn = 0;
@@ -2192,9 +2408,10 @@ extern "C" int attnres_init(int device) {
   if (e != hipSuccess) return hip_fail(e);
   if (device >= n) return ATTNRES_E_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  const int rc = init_device_locked(device);
-  if (rc != ATTNRES_OK) return rc;
-  return static_scratch_locked(device);
+  int rc = init_device_locked(device);
+  if (rc == ATTNRES_OK) rc = static_scratch_locked(device);
+  if (rc == ATTNRES_OK && ATTNRES_ANYH_STAGED) rc = allow_staged_lds();
+  return rc;
 }
 
 extern "C" void attnres_shutdown(void) {

@@ -184,6 +184,35 @@ def test_any_h_rows_in_lds(G, kw):
         G.check_full(inp, G.download(d), ref)
 
 
+# The any-H kernel with three bank rows staged into LDS through registers:
+# four segments per lane, 4..8 bank rows, in 5 waves (H = 8200..10240) for
+# more tokens than compute units (T > 256 on 256 CUs), in 6 waves (H =
+# 10248..12288) for up to two per CU (T = 257..512); masked rows, and the
+# cached-read form (T * H >= 1024 * 7168 with a delta and a written slot).
+STAGED_CASES = [
+    dict(H=10240, T=800, nb=8, widx=3),                          # cached rewritten rows
+    dict(H=12288, T=300, nb=4, has_onorm=False, widx=-1),       # 6 waves
+    dict(H=10240, T=400, nb=6, has_delta=False, widx=5),
+    dict(H=9000, T=500, nb=7, widx=0),                           # masked
+    dict(H=12280, T=260, nb=5, has_delta=False, has_onorm=False),  # 6 waves, masked
+    dict(H=9992, T=800, nb=8, widx=7, recipe="soft", token_pad=64),  # masked and cached
+    dict(H=11264, T=512, nb=6, has_delta=False, widx=-1),       # 6 waves, masked, two per CU
+    dict(H=8200, T=257, nb=4),                                   # first four-segment size
+]
+
+
+@pytest.mark.parametrize("kw", STAGED_CASES, ids=lambda kw: "_".join(f"{k}{v}" for k, v in kw.items()))
+def test_any_h_rows_staged_in_lds(G, kw):
+    case = W.Case("staged_rows_" + "_".join(f"{k}{v}" for k, v in kw.items()), seed=78, **kw)
+    inp = W.make_inputs(case)
+    ref = G.oracle_full_threaded(inp)
+    for path in (None, A_PATH_ANY_H):
+        G.say(case.name, "path", path)
+        d = G.upload(inp)
+        G.run(d, path=path)
+        G.check_full(inp, G.download(d), ref)
+
+
 @pytest.mark.parametrize("case", W.variant_matrix(), ids=lambda c: c.name)
 def test_variant_matrix(G, case):
     inp = W.make_inputs(case)

@@ -63,7 +63,19 @@ def test_any_h_lds_row_variant_fits_four_workgroups_per_cu(tmp_path):
     per SIMD).  Only two segments per lane are built that way."""
     ks = _kernels(tmp_path)
     lds = {n: k for n, k in ks.items()
-           if "attnres_anyh_kernel" in n and n.endswith("Li3EEEvNS0_7KParamsE")}
+           if "attnres_anyh_kernel" in n and n.endswith("Li3ELb0EEEvNS0_7KParamsE")}
     assert len(lds) == 2 * 5 * 8  # masked or not x nb 4..8 x (delta, norm, cached)
     assert all("ILi2E" in n for n in lds), "LDS rows are built for two segments per lane only"
     assert all(k["vgprs"] <= 96 for k in lds.values()), lds
+
+
+def test_any_h_staged_variant_fits_two_workgroups_per_cu(tmp_path):
+    """The any-H kernel that stages three bank rows into LDS exists to let two
+    6-wave workgroups of four segments per lane share a compute unit, which
+    needs at most 168 VGPRs (three waves per SIMD)."""
+    ks = _kernels(tmp_path)
+    stg = {n: k for n, k in ks.items()
+           if "attnres_anyh_kernel" in n and n.endswith("Li3ELb1EEEvNS0_7KParamsE")}
+    assert len(stg) == 2 * 5 * 8  # masked or not x nb 4..8 x (delta, norm, cached)
+    assert all("ILi4E" in n for n in stg), "staging is built for four segments per lane only"
+    assert all(k["vgprs"] <= 168 for k in stg.values()), stg
