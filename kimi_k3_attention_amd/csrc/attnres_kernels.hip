@@ -77,7 +77,7 @@
 #define ATTNRES_SPLIT_MFMA_WORDS 40     // split path: from this many words, one matrix-core product
 #endif
 #ifndef ATTNRES_ANYH_STAGED
-#define ATTNRES_ANYH_STAGED 1           // any-H, four segments: three bank rows staged in LDS
+#define ATTNRES_ANYH_STAGED 1           // any-H: three bank rows staged in LDS where it pays
 #endif
 #ifndef ATTNRES_CUR_FIRST
 #define ATTNRES_CUR_FIRST 1             // issue prefix and delta before the bank rows
@@ -249,25 +249,24 @@ __device__ __forceinline__ float lane_shuffle(float v, int src) {
 // (needed whenever a logit is formed: with bank rows, or in the second
 // kernel of the two-kernel form, which scores cur alone).
 //
-// LR > 0: the first LR sources (bank rows) go straight from memory into LDS
-// (global_load_lds, 16 bytes per lane, no registers), issued after every
-// other row; they are read back from LDS when used.  That frees 4 SPL
-// registers per row, so more workgroups fit a CU (see the any-H kernel).
-// STG (with LR > 0): the LR rows are staged instead.  They are loaded into
-// registers right after cur's rows, their partials are taken as they land,
-// and then each lane copies them to LDS.  Only then are the last bank rows
-// issued (issue_rest), into the registers the staged rows held.  Every load
-// is a plain one, so the waits stay progressive; with LDS-direct loads in
-// flight the compiler waits for all loads at the first use of any.
+// LR > 0 (STG): the first LR sources (bank rows) are staged into LDS, which
+// frees 4 SPL registers per row, so that more workgroups fit a CU (see the
+// any-H kernel).  They are loaded into registers right after cur's rows,
+// their partials are taken as they land, and then each lane copies them to
+// its own LDS slots, from which the mixture reads them.  The other bank rows
+// are issued as registers free up (issue_rest).  Every load is a plain one,
+// so the waits stay progressive: with LDS-direct loads (global_load_lds) in
+// flight, the compiler waits for every load at the first use of any.
 template <int NB, bool DELTA, bool ONORM, int SPL, bool MASKED = false, bool CACHE_RW = false,
-          bool CUR = true, bool Q = (NB > 0), int LR = 0, bool STG = false>
+          bool CUR = true, bool Q = (NB > 0), int LR = 0>
 struct Token {
   static constexpr int NS = NB + (CUR ? 1 : 0);
+  static constexpr bool STG = LR > 0;
   static_assert(LR == 0 || (CUR && LR < NB), "LDS rows are bank rows of a full token");
-  static_assert(!STG || LR > 0, "staging needs LDS rows");
   // STG: bank rows (in issue order) of the first burst, the staged ones;
   // the rest follow the staging.  With cur's two rows and the weights that
-  // is what four segments per lane leave room for at 168 VGPRs.
+  // is what the register budgets leave room for (96 VGPRs at two segments
+  // per lane, 168 at four).
   static constexpr int kFirst = STG ? LR : NB;
   u32x4 rms[SPL], res[SPL], onw[SPL];  // weights
   u32x4 x[NB + 1][SPL];                // bank slots 0..NB-1, then prefix (cur after finish_cur)
@@ -280,18 +279,8 @@ struct Token {
   // masked row's end: staged rows carry the zeros their loads gave), else
   // from registers.
   __device__ __forceinline__ u32x4 row(int j, int i) const {
-    if (j < LR) {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      const u32x4 v = lds_rows[(j * SPL + i) * nthr + int(threadIdx.x)];
-      return MASKED && !STG && !seg_ok[i] ? zero : v;
-    }
+    if (j < LR) return lds_rows[(j * SPL + i) * nthr + int(threadIdx.x)];
     return x[j][i];
-  }
-  // The LDS rows are written by the memory system behind the compiler's
-  // back: wait for every load in flight before reading them.  (Staged rows
-  // are written by the lanes themselves, which the compiler tracks.)
-  __device__ __forceinline__ static void wait_lds_rows() {
-    if constexpr (LR > 0 && !STG) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
   // STG: staged row k from this lane's registers to its own LDS slots.
   __device__ __forceinline__ void stage(int k) {
@@ -485,7 +474,7 @@ struct Token {
       // in flight, and every source's arithmetic would wait for all of them.
       static_assert(NB > 0, "a rewritten source row needs a source slot");
 #pragma unroll
-      for (int k = LR; k + 1 < NB; ++k) {
+      for (int k = 0; k + 1 < NB; ++k) {
         const int slot = k + (k >= p.widx ? 1 : 0);
         const uint16_t *row = bank + slot * p.slot_stride;
 #pragma unroll
@@ -503,7 +492,7 @@ struct Token {
       // them by when their addresses are ready), so that the partials of each
       // source can start as soon as its own rows land.
 #pragma unroll
-      for (int j = LR; j < NB; ++j) {
+      for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
           x[j][i] = load_row(p, bank + j * p.slot_stride, sb[i], ok[i]);
@@ -511,26 +500,6 @@ struct Token {
       }
     }
     if constexpr (!kCurFirst) issue_cur(p, t, prow, sb, ok);
-    if constexpr (LR > 0) {
-      // The first LR sources last, straight into LDS: in the cached variant
-      // the first LR of the ascending slots other than widx, else slots
-      // 0..LR-1.  Each wave writes 64 consecutive 16-byte slots.
-      __builtin_amdgcn_sched_barrier(0);
-      const int wave_base = int(threadIdx.x) & ~(kWave - 1);
-#pragma unroll
-      for (int k = 0; k < LR; ++k) {
-        const int slot = CACHE_RW ? k + (k >= p.widx ? 1 : 0) : k;
-        const uint16_t *rowp = bank + slot * p.slot_stride;
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) {
-          u32x4 *dst = lds_rows + (k * SPL + i) * nthr + wave_base;
-          if (!MASKED || ok[i])
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)at(rowp, sb[i]),
-                (__attribute__((address_space(3))) void *)dst, 16, 0, ATTNRES_NT_LOADS ? 2 : 0);
-        }
-      }
-    }
     // Keep the scheduler from sinking any of these loads below the arithmetic.
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -987,18 +956,17 @@ __device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
 // SPL >= p.nseg.  With two segments per lane a token fits 128 VGPRs (four
 // waves per SIMD); four segments may take 256.
 //
-// LR > 0 (kAnyLdsRows bank rows in LDS, launched with LR * SPL * blockDim.x
-// * 16 bytes of dynamic LDS): the same steps with those rows held in LDS
-// instead of registers, for one more resident workgroup per CU where the
-// registers are what limits it (see anyh_lds_rows).  STG: those rows reach
-// LDS through registers (staged; see Token), not by LDS-direct loads.
-template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, int LR = 0,
-          bool STG = false>
+// LR > 0 (kAnyLdsRows bank rows staged in LDS, launched with LR * SPL *
+// blockDim.x * 16 bytes of dynamic LDS): the same steps with those rows held
+// in LDS instead of registers, for one more resident workgroup per CU where
+// the registers are what limits it (see anyh_lds_rows).
+template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, int LR = 0>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWave, kAnyMaxThreads),
                                amdgpu_waves_per_eu(LR == 0 ? (SPL <= 2 ? 4 : 2)
                                                            : (SPL <= 2 ? 5 : 3))))
 attnres_anyh_kernel(KParams p) {
   constexpr int NS = NB + 1;
+  constexpr bool STG = LR > 0;
   __shared__ __align__(16) float s_part[2 * NS][kAnyMaxRows];
   __shared__ __align__(16) float s_ysq[kAnyMaxRows];
   extern __shared__ __align__(16) u32x4 s_rows[];
@@ -1013,7 +981,7 @@ attnres_anyh_kernel(KParams p) {
   const int seg0 = int(threadIdx.x);  // whole-line loads, as in the row kernel
   const int seg_step = nthreads;
 
-  Token<NB, DELTA, ONORM, SPL, MASKED, CACHE_RW, true, (NB > 0), LR, STG> tk;
+  Token<NB, DELTA, ONORM, SPL, MASKED, CACHE_RW, true, (NB > 0), LR> tk;
   tk.lds_rows = s_rows;
   tk.nthr = p.threads;
   tk.issue(p, t, seg0, seg_step);
@@ -1037,15 +1005,13 @@ attnres_anyh_kernel(KParams p) {
   tk.query(qh, ql);
 
   // Each source's partials as its rows land, in issue order as in the row
-  // kernel; then the LDS rows, issued last, once every load has landed.
-  // STG: cur, then bank rows in order; a staged row goes to LDS right after
-  // its partials, and each step releases the next loads (issue_rest).
+  // kernel.  STG: cur, then bank rows in order; a staged row goes to LDS
+  // right after its partials, and each step releases the next loads
+  // (issue_rest).
 #pragma unroll
-  for (int j = STG ? 0 : LR; j < NS + (STG ? 0 : LR); ++j) {
-    const int src0 = j < NS ? j : j - NS;
-    const int src = decltype(tk)::kCurFirst ? (j == 0 ? NB : j - 1) : src0;
+  for (int j = 0; j < NS; ++j) {
+    const int src = decltype(tk)::kCurFirst ? (j == 0 ? NB : j - 1) : j;
     if (src == NB) tk.finish_cur();
-    if (j == NS) tk.wait_lds_rows();
     float sj, dj;
     if (STG && src < LR)
       tk.template partial<true>(src, qh, ql, sj, dj);
@@ -1679,30 +1645,33 @@ KernelFn anyh_fn(bool d, bool o, bool cache_rw) {
            : attnres_anyh_kernel<SPL, MASKED, NB, false, false>;
 }
 
-// The any-H kernel with kAnyLdsRows bank rows in LDS (4..8 bank rows).
+// The any-H kernel with kAnyLdsRows bank rows staged into LDS (4..8 bank
+// rows, two or four segments per lane).
 constexpr int kAnyLdsRows = 3;
 template <int SPL, bool MASKED, int NB>
 KernelFn anyh_lds_fn(bool d, bool o, bool c) {
   if constexpr (NB >= 4) {
+    constexpr int L = kAnyLdsRows;
     if (c) {
       if (d)
-        return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, true, kAnyLdsRows>
-                 : attnres_anyh_kernel<SPL, MASKED, NB, true, false, true, kAnyLdsRows>;
-      return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, true, kAnyLdsRows>
-               : attnres_anyh_kernel<SPL, MASKED, NB, false, false, true, kAnyLdsRows>;
+        return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, true, L>
+                 : attnres_anyh_kernel<SPL, MASKED, NB, true, false, true, L>;
+      return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, true, L>
+               : attnres_anyh_kernel<SPL, MASKED, NB, false, false, true, L>;
     }
     if (d)
-      return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, false, kAnyLdsRows>
-               : attnres_anyh_kernel<SPL, MASKED, NB, true, false, false, kAnyLdsRows>;
-    return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, false, kAnyLdsRows>
-             : attnres_anyh_kernel<SPL, MASKED, NB, false, false, false, kAnyLdsRows>;
+      return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, false, L>
+               : attnres_anyh_kernel<SPL, MASKED, NB, true, false, false, L>;
+    return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, false, L>
+             : attnres_anyh_kernel<SPL, MASKED, NB, false, false, false, L>;
   }
   return nullptr;
 }
 template <int NB>
 KernelFn anyh_lds_pick(const AnyShape &sh, bool d, bool o, bool c) {
-  if (sh.spl != 2) return nullptr;
-  return sh.masked ? anyh_lds_fn<2, true, NB>(d, o, c) : anyh_lds_fn<2, false, NB>(d, o, c);
+  if (sh.spl == 2)
+    return sh.masked ? anyh_lds_fn<2, true, NB>(d, o, c) : anyh_lds_fn<2, false, NB>(d, o, c);
+  return sh.masked ? anyh_lds_fn<4, true, NB>(d, o, c) : anyh_lds_fn<4, false, NB>(d, o, c);
 }
 KernelFn pick_anyh_lds(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw) {
   switch (nb) {
@@ -1714,80 +1683,41 @@ KernelFn pick_anyh_lds(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw
   }
 }
 
-// The any-H kernel with kAnyLdsRows bank rows staged into LDS through
-// registers (four segments per lane, 4..8 bank rows).
-template <bool MASKED, int NB>
-KernelFn anyh_staged_fn(bool d, bool o, bool c) {
-  if constexpr (NB >= 4) {
-    constexpr int L = kAnyLdsRows;
-    if (c) {
-      if (d)
-        return o ? attnres_anyh_kernel<4, MASKED, NB, true, true, true, L, true>
-                 : attnres_anyh_kernel<4, MASKED, NB, true, false, true, L, true>;
-      return o ? attnres_anyh_kernel<4, MASKED, NB, false, true, true, L, true>
-               : attnres_anyh_kernel<4, MASKED, NB, false, false, true, L, true>;
-    }
-    if (d)
-      return o ? attnres_anyh_kernel<4, MASKED, NB, true, true, false, L, true>
-               : attnres_anyh_kernel<4, MASKED, NB, true, false, false, L, true>;
-    return o ? attnres_anyh_kernel<4, MASKED, NB, false, true, false, L, true>
-             : attnres_anyh_kernel<4, MASKED, NB, false, false, false, L, true>;
-  }
-  return nullptr;
-}
-KernelFn pick_anyh_staged(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw) {
-  if (sh.spl != 4) return nullptr;
-  switch (nb) {
-#define ATTNRES_CASE(N)                                              \
-  case N:                                                            \
-    return sh.masked ? anyh_staged_fn<true, N>(d, o, cache_rw)       \
-                     : anyh_staged_fn<false, N>(d, o, cache_rw);
-    ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
-#undef ATTNRES_CASE
-    default: return nullptr;
-  }
-}
-
-// Whether an any-H call holds kAnyLdsRows bank rows in LDS, and the dynamic
-// LDS bytes it then takes.  Registers bound the resident workgroups per CU of
-// the plain kernel: at two segments per lane it may take 128 VGPRs (four
-// waves per SIMD), so three 5-wave workgroups fit (H = 4104..5120), and a
-// call of more tokens than that runs a partial second round (T = 1024 at
-// H = 5120: 768 + 256).  With three bank rows out of the registers the kernel
-// is built for 96 VGPRs and four fit, 1024 per round.  The rows then take
-// 30 KB of LDS per workgroup (4 x 32 KB of a CU's 160 KB).  Its cost: with
-// loads into LDS in flight the compiler waits for every load before the first
-// arithmetic, so no source's arithmetic overlaps the later rows' arrival.
-// Measured (T = 1024, delta and norm, µs per call, plain / LDS rows): H = 5120
-// nb = 5 22.6 / 20.4, nb = 7 26.6 / 23.2, nb = 8 28.8 / 27.0; where the extra
-// workgroup did not change the rounds it lost: H = 6144 (6 waves, two to four
-// per CU) nb = 6 27.5 / 30.3, H = 10240 and 12288 (four segments, one to two
-// per CU) +11-13 %.  So only 5-wave workgroups with 4 or more bank rows, and
-// only when the tokens exceed the plain kernel's three per CU.
+// Whether an any-H call stages kAnyLdsRows bank rows into LDS, and the
+// dynamic LDS bytes it then takes.  Registers bound the resident workgroups
+// per CU of the plain kernel; staging three rows frees 12 (two segments per
+// lane) or 48 (four) VGPRs per lane for one more workgroup, at the cost of a
+// second round of loads per token (the rows after the staged ones wait for
+// registers).
+// - Two segments per lane: the plain kernel may take 128 VGPRs (four waves
+//   per SIMD), so three 5-wave workgroups fit (H = 4104..5120), and a call of
+//   more tokens than that runs a partial second round (T = 1024 at H = 5120:
+//   768 + 256).  Staged, the kernel is built for 96 VGPRs and four fit, with
+//   30 KB of LDS each.  Measured (T = 1024, delta and norm, µs per call,
+//   plain / LDS-direct rows / staged): H = 5120 nb = 8 28.6 / 24.8 / 23.6,
+//   nb = 4 19.9 / 18.6 / 18.9; H = 4104 nb = 8 - / 22.8 / 21.7; T = 2048
+//   H = 4608 - / 45.1 / 42.5.  With a sixth wave the extra workgroup did not
+//   change the rounds and the lost overlap cost more (H = 6144, LDS-direct
+//   rows: +10 %).  So 5-wave workgroups, for more tokens than three per CU.
+// - Four segments per lane: a token of 5-6 waves (H = 8200..12288) fills a
+//   CU's registers (200+ VGPRs), one workgroup per CU; staged it takes at
+//   most 168 (three waves per SIMD), so two fit, with 61-74 KB of LDS each.
+//   Measured (delta, norm, 8 bank rows, µs per call, plain / staged): 5
+//   waves, H = 8704 T = 300 22.3 / 21.2, T = 1024 53.7 / 51.7, T = 2048
+//   97.5 / 94.2; H = 9216 T = 4096 without delta or norm 150.7 / 141.9;
+//   H = 10240 T = 300 23.5 / 22.5, T = 2048 103.7 / 105.9.  6 waves,
+//   H = 12288: T = 300 26.0 / 25.3, T = 1024 64.8 / 65.6, T = 2048 119.2 /
+//   121.8 (H = 11264 and 12032 alike).  So 5-wave workgroups from one token
+//   per CU up, 6-wave ones only up to two.
 bool anyh_lds_rows(const AnyShape &sh, int64_t T, int nb, int cus, size_t *dyn) {
   const int waves = sh.threads / kWave;
-  if (sh.spl != 2 || waves != 5 || nb < 4 || T <= int64_t(3) * cus) return false;
-  *dyn = size_t(kAnyLdsRows) * sh.spl * sh.threads * 16;
-  return true;
-}
-
-// Whether an any-H call stages kAnyLdsRows bank rows into LDS, and the
-// dynamic LDS bytes it then takes.  At four segments per lane a token of
-// 5-6 waves (H = 8200..12288) fills a CU's registers (200+ VGPRs), one
-// workgroup per CU.  Staging three rows brings it under 168 (three waves per
-// SIMD), so two fit, with 61-74 KB of LDS each.  The cost is a second round
-// of loads per token (the rows after the staged ones wait for registers).
-// Measured (delta, norm, 8 bank rows, µs per call, plain / staged): 5 waves,
-// H = 8704 T = 300 22.3 / 21.2, T = 1024 53.7 / 51.7, T = 2048 97.5 / 94.2;
-// H = 9216 T = 4096 without delta or norm 150.7 / 141.9; H = 10240 T = 300
-// 23.5 / 22.5, T = 2048 103.7 / 105.9.  6 waves, H = 12288: T = 300 26.0 /
-// 25.3, T = 1024 64.8 / 65.6, T = 2048 119.2 / 121.8 (H = 11264 and 12032
-// alike).  So 5-wave workgroups from one token per CU up, 6-wave ones only
-// up to two.
-bool anyh_staged_rows(const AnyShape &sh, int64_t T, int nb, int cus, size_t *dyn) {
-  const int waves = sh.threads / kWave;
-  if (sh.spl != 4 || nb < 4 || T <= int64_t(cus)) return false;
-  if (waves > 6 || (waves == 6 && T > int64_t(2) * cus)) return false;
+  if (!ATTNRES_ANYH_STAGED || nb < 4) return false;
+  bool use;
+  if (sh.spl == 2)
+    use = waves == 5 && T > int64_t(3) * cus;
+  else
+    use = T > int64_t(cus) && (waves == 5 || (waves == 6 && T <= int64_t(2) * cus));
+  if (!use) return false;
   *dyn = size_t(kAnyLdsRows) * sh.spl * sh.threads * 16;
   return true;
 }
@@ -2066,16 +1996,19 @@ int allow_dynamic_lds(KernelFn fn, size_t bytes) {
   return ATTNRES_OK;
 }
 
-// The dynamic-LDS attribute of every staged any-H kernel, so that a first
-// call under graph capture makes no attribute call.
+// The dynamic-LDS attribute of every any-H kernel with staged rows, so that
+// a first call under graph capture makes no attribute call.  The largest
+// such workgroup (384 lanes, four segments) takes 72 KB.
+constexpr size_t kAnyLdsMaxBytes = size_t(kAnyLdsRows) * 4 * 384 * 16;
 int allow_staged_lds() {
-  const AnyShape shapes[2] = {{4, 6 * kWave, false}, {4, 6 * kWave, true}};
+  const AnyShape shapes[4] = {
+      {2, 5 * kWave, false}, {2, 5 * kWave, true}, {4, 6 * kWave, false}, {4, 6 * kWave, true}};
   for (const AnyShape &sh : shapes)
     for (int nb = 4; nb <= kMaxBlocks; ++nb)
       for (int f = 0; f < 8; ++f) {
-        const KernelFn fn = pick_anyh_staged(sh, nb, f & 1, f & 2, f & 4);
+        const KernelFn fn = pick_anyh_lds(sh, nb, f & 1, f & 2, f & 4);
         if (!fn) continue;
-        const int rc = allow_dynamic_lds(fn, size_t(kAnyLdsRows) * 4 * 384 * 16);
+        const int rc = allow_dynamic_lds(fn, kAnyLdsMaxBytes);
         if (rc != ATTNRES_OK) return rc;
       }
   return ATTNRES_OK;
@@ -2189,13 +2122,9 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
     size_t dyn = 0;
     KernelFn fn = nullptr;
     if (anyh_lds_rows(sh, a.T, a.num_blocks, cus, &dyn)) {
-      // at most 30 KB of dynamic LDS (320 lanes), under the default limit
       fn = pick_anyh_lds(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
-    } else if (ATTNRES_ANYH_STAGED && anyh_staged_rows(sh, a.T, a.num_blocks, cus, &dyn)) {
-      fn = pick_anyh_staged(sh, a.num_blocks, has_d, has_o, cache_rewritten(a));
       if (fn) {
-        // the largest such workgroup (384 lanes) takes 72 KB
-        rc = allow_dynamic_lds(fn, size_t(kAnyLdsRows) * 4 * 384 * 16);
+        rc = allow_dynamic_lds(fn, kAnyLdsMaxBytes);
         if (rc != ATTNRES_OK) return rc;
       }
     }

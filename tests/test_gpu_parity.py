@@ -157,10 +157,10 @@ def test_long_prefill_full(G, T):
     assert (got.bank == inp.bank).all(), "bank (or its padding) modified"
 
 
-# The any-H kernel with three bank rows in LDS: 5-wave workgroups (H 4104..5120),
-# 4..8 bank rows, more tokens than three per compute unit (T > 768 on 256 CUs);
-# masked rows, and the cached-read form (T * H >= 1024 * 7168 with a delta and
-# a written source slot).
+# The any-H kernel with three bank rows staged in LDS, two segments per lane:
+# 5-wave workgroups (H 4104..5120), 4..8 bank rows, more tokens than three per
+# compute unit (T > 768 on 256 CUs); masked rows, and the cached-read form
+# (T * H >= 1024 * 7168 with a delta and a written source slot).
 LDS_ROW_CASES = [
     dict(H=5120, T=1024, nb=8, widx=3),
     dict(H=5120, T=1000, nb=4, has_onorm=False, widx=-1),
@@ -184,11 +184,11 @@ def test_any_h_rows_in_lds(G, kw):
         G.check_full(inp, G.download(d), ref)
 
 
-# The any-H kernel with three bank rows staged into LDS through registers:
-# four segments per lane, 4..8 bank rows, in 5 waves (H = 8200..10240) for
-# more tokens than compute units (T > 256 on 256 CUs), in 6 waves (H =
-# 10248..12288) for up to two per CU (T = 257..512); masked rows, and the
-# cached-read form (T * H >= 1024 * 7168 with a delta and a written slot).
+# The same with four segments per lane: 4..8 bank rows, in 5 waves (H =
+# 8200..10240) for more tokens than compute units (T > 256 on 256 CUs), in 6
+# waves (H = 10248..12288) for up to two per CU (T = 257..512); masked rows,
+# and the cached-read form (T * H >= 1024 * 7168 with a delta and a written
+# slot).
 STAGED_CASES = [
     dict(H=10240, T=800, nb=8, widx=3),                          # cached rewritten rows
     dict(H=12288, T=300, nb=4, has_onorm=False, widx=-1),       # 6 waves

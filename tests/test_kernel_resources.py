@@ -57,25 +57,17 @@ def test_row_kernel_fits_two_workgroups_per_cu(tmp_path):
     assert all(k["vgprs"] <= 128 for k in row.values()), row
 
 
-def test_any_h_lds_row_variant_fits_four_workgroups_per_cu(tmp_path):
-    """The any-H kernel with three bank rows in LDS exists to let four 5-wave
-    workgroups share a compute unit, which needs at most 96 VGPRs (five waves
-    per SIMD).  Only two segments per lane are built that way."""
-    ks = _kernels(tmp_path)
-    lds = {n: k for n, k in ks.items()
-           if "attnres_anyh_kernel" in n and n.endswith("Li3ELb0EEEvNS0_7KParamsE")}
-    assert len(lds) == 2 * 5 * 8  # masked or not x nb 4..8 x (delta, norm, cached)
-    assert all("ILi2E" in n for n in lds), "LDS rows are built for two segments per lane only"
-    assert all(k["vgprs"] <= 96 for k in lds.values()), lds
-
-
-def test_any_h_staged_variant_fits_two_workgroups_per_cu(tmp_path):
-    """The any-H kernel that stages three bank rows into LDS exists to let two
-    6-wave workgroups of four segments per lane share a compute unit, which
-    needs at most 168 VGPRs (three waves per SIMD)."""
+def test_any_h_staged_variants_fit_one_more_workgroup_per_cu(tmp_path):
+    """The any-H kernel with three bank rows staged in LDS exists to fit one
+    more workgroup per compute unit: four 5-wave workgroups at two segments
+    per lane need at most 96 VGPRs (five waves per SIMD), two 5- or 6-wave
+    ones at four segments at most 168 (three waves per SIMD)."""
     ks = _kernels(tmp_path)
     stg = {n: k for n, k in ks.items()
-           if "attnres_anyh_kernel" in n and n.endswith("Li3ELb1EEEvNS0_7KParamsE")}
-    assert len(stg) == 2 * 5 * 8  # masked or not x nb 4..8 x (delta, norm, cached)
-    assert all("ILi4E" in n for n in stg), "staging is built for four segments per lane only"
-    assert all(k["vgprs"] <= 168 for k in stg.values()), stg
+           if "attnres_anyh_kernel" in n and n.endswith("Li3EEEvNS0_7KParamsE")}
+    two = {n: k for n, k in stg.items() if "anyh_kernelILi2E" in n}
+    four = {n: k for n, k in stg.items() if "anyh_kernelILi4E" in n}
+    # each: masked or not x nb 4..8 x (delta, norm, cached)
+    assert len(two) == len(four) == 2 * 5 * 8 and len(stg) == 2 * 2 * 5 * 8, len(stg)
+    assert all(k["vgprs"] <= 96 for k in two.values()), two
+    assert all(k["vgprs"] <= 168 for k in four.values()), four
