@@ -1696,9 +1696,14 @@ KernelFn pick_anyh_lds(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw
 //   30 KB of LDS each.  Measured (T = 1024, delta and norm, µs per call,
 //   plain / LDS-direct rows / staged): H = 5120 nb = 8 28.6 / 24.8 / 23.6,
 //   nb = 4 19.9 / 18.6 / 18.9; H = 4104 nb = 8 - / 22.8 / 21.7; T = 2048
-//   H = 4608 - / 45.1 / 42.5.  With a sixth wave the extra workgroup did not
-//   change the rounds and the lost overlap cost more (H = 6144, LDS-direct
-//   rows: +10 %).  So 5-wave workgroups, for more tokens than three per CU.
+//   H = 4608 - / 45.1 / 42.5.  With a sixth wave (two plain workgroups per
+//   CU, three staged), plain / staged: H = 5632 (masked) T = 600 18.3 /
+//   18.6, T = 1024 30.7 / 26.1, T = 2048 53.2 / 50.7; H = 6144 T = 600 19.1 /
+//   22.2, T = 1024 32.1 / 33.5, T = 2048 55.7 / 55.4 (yet nb = 4 24.0 / 21.2).
+//   Staging lost where a row is a whole number of 4 KB (H = 6144, 10240,
+//   12288), perhaps from how the rows fall on the memory channels (not
+//   measured), and won elsewhere.  So 5-wave workgroups, and 6-wave ones
+//   over masked rows, for more tokens than three per CU.
 // - Four segments per lane: a token of 5-6 waves (H = 8200..12288) fills a
 //   CU's registers (200+ VGPRs), one workgroup per CU; staged it takes at
 //   most 168 (three waves per SIMD), so two fit, with 61-74 KB of LDS each.
@@ -1714,7 +1719,7 @@ bool anyh_lds_rows(const AnyShape &sh, int64_t T, int nb, int cus, size_t *dyn) 
   if (!ATTNRES_ANYH_STAGED || nb < 4) return false;
   bool use;
   if (sh.spl == 2)
-    use = waves == 5 && T > int64_t(3) * cus;
+    use = (waves == 5 || (waves == 6 && sh.masked)) && T > int64_t(3) * cus;
   else
     use = T > int64_t(cus) && (waves == 5 || (waves == 6 && T <= int64_t(2) * cus));
   if (!use) return false;
