@@ -132,8 +132,8 @@ int validate(const FwdArgs &a) {
     if ((a.block_token_stride % 8) != 0 || (a.block_slot_stride % 8) != 0) return ATTNRES_E_ALIGN;
     if (!bank_rows_disjoint(a.T, a.block_token_stride, a.max_blocks, a.block_slot_stride, a.H))
       return ATTNRES_E_STRIDE;
-    bank_bytes = 2 * (static_cast<i128>(a.T - 1) * a.block_token_stride +
-                      static_cast<i128>(a.max_blocks - 1) * a.block_slot_stride + a.H);
+    bank_bytes = 2 * ((static_cast<i128>(a.T) - 1) * a.block_token_stride +
+                      (static_cast<i128>(a.max_blocks) - 1) * a.block_slot_stride + a.H);
   }
 
   const i128 row_bytes = 2 * static_cast<i128>(a.H);
@@ -181,8 +181,8 @@ int validate_partial(const FwdArgs &a, const void *partial, int64_t bytes) {
   };
   i128 bank_bytes = 0;
   if (bank_used)
-    bank_bytes = 2 * (static_cast<i128>(a.T - 1) * a.block_token_stride +
-                      static_cast<i128>(a.max_blocks - 1) * a.block_slot_stride + a.H);
+    bank_bytes = 2 * ((static_cast<i128>(a.T) - 1) * a.block_token_stride +
+                      (static_cast<i128>(a.max_blocks) - 1) * a.block_slot_stride + a.H);
   const Rows r[7] = {
       mat(a.prefix, a.prefix_stride), mat(a.delta, a.delta_stride),
       rows(bank_used ? a.blocks : nullptr, 1, 0, bank_bytes, false),

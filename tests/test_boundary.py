@@ -373,6 +373,32 @@ def test_plain_c_caller_builds_and_links():
     assert res.returncode == 2, res.stdout + res.stderr
 
 
+def test_validation_under_sanitizers(tmp_path):
+    """The host-side checks (kimi_k3_attention_amd/csrc/attnres_validate.cpp,
+    plain C++), built with g++ under the address and undefined-behaviour
+    sanitizers, through tests/c/validate_fuzz.cpp: 600,000 calls with
+    plausible and extreme sizes, strides, indices, epsilons and pointers
+    return only documented statuses, with no overflow or bad access."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not installed")
+    exe = str(tmp_path / "validate_fuzz")
+    src = os.path.join(ROOT, "kimi_k3_attention_amd", "csrc")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"), "-I", src,
+           os.path.join(src, "attnres_validate.cpp"),
+           os.path.join(ROOT, "tests", "c", "validate_fuzz.cpp"), "-o", exe]
+    build = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    if build.returncode != 0 and "asan" in (build.stderr or "").lower():
+        pytest.skip("the sanitizer runtime is not installed: " + build.stderr[-300:])
+    assert build.returncode == 0, build.stderr
+    # (another preloaded library may come before the sanitizer's runtime)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:verify_asan_link_order=0")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    assert res.returncode == 0 and res.stdout.startswith("ok "), res.stdout + res.stderr
+
+
 def test_partial_bytes(A):
     """The two-kernel form's state: fp32 [T, H] plus two fp32 per token."""
     lib = A.lib()
