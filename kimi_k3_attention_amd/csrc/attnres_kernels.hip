@@ -237,12 +237,13 @@ __device__ __forceinline__ float lane_shuffle(float v, int src) {
 // One token's data for SPL segments per lane: segment i of this lane is
 // seg0 + i * seg_step.  Everything is issued in one burst: the L2-resident
 // weights first (the wait counter is in order, so the query can be formed
-// while the rows are still in flight), then the bank rows, prefix and delta.
+// while the rows are still in flight), then the rows: prefix and delta
+// before the bank rows (kCurFirst, from three bank rows up) or after them.
 // Row bases are workgroup-uniform (scalar registers); lanes add their
 // 16-byte segment offsets.
 //
 // MASKED (rows whose length is not a multiple of the workgroup's reach):
-// a segment at or past p.nseg loads nothing and holds zeros, which add
+// a segment at or past p.nseg reads zero (a range-checked load), which adds
 // nothing to any sum, and is never stored.
 // CUR = false: the bank rows only (the first kernel of the two-kernel form),
 // no prefix, delta or cur.  Q: load the scoring weights for the fused query
