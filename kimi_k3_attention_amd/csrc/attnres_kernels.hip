@@ -331,10 +331,13 @@ struct Token {
         const_cast<uint16_t *>(row), 0, p.nseg * kSeg * int(sizeof(uint16_t)), kBufferFormat);
     return __builtin_amdgcn_raw_buffer_load_b128(r, int(b), 0, AUX);
   }
+  // (Staged tokens take the buffer form whether masked or not: it holds fewer
+  // registers, which decides how many of their workgroups fit a CU.)
+  static constexpr bool kBufferRows = MASKED || STG;
   __device__ __forceinline__ static u32x4 load_row(const KParams &p, const uint16_t *row,
                                                    uint32_t b, bool ok) {
     (void)ok;
-    if constexpr (MASKED) return load_in_row<ATTNRES_NT_LOADS ? kAuxNt : 0>(p, row, b);
+    if constexpr (kBufferRows) return load_in_row<ATTNRES_NT_LOADS ? kAuxNt : 0>(p, row, b);
     return load_stream(at(row, b));
   }
   // With CACHE_RW, the rows a call also writes (the bank slot widx, a source
@@ -672,17 +675,31 @@ struct Token {
   // only rewrites elements it has read itself; the writes go out once all of
   // its loads have completed: with out, or right after the last source's
   // partials, whose wait retires every earlier load (after_partials).
+  // A row's segment at byte offset b, written.  MASKED: a buffer store whose
+  // record is the row, so a segment past the row's end is dropped by the
+  // hardware's range check, with no branch (as for the loads).
+  template <bool NT>
+  __device__ __forceinline__ static void store_row(const KParams &p, uint16_t *row, uint32_t b,
+                                                   u32x4 v) {
+    if constexpr (kBufferRows) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          row, 0, p.nseg * kSeg * int(sizeof(uint16_t)), kBufferFormat);
+      __builtin_amdgcn_raw_buffer_store_b128(v, r, int(b), 0, NT ? kAuxNt : 0);
+    } else {
+      store_stream<NT>(at(row, b), v);
+    }
+  }
+
   __device__ __forceinline__ void store_cur(const KParams &p, int64_t t, int seg0,
                                             int seg_step) const {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
-      if (!in_row(p, seg0 + i * seg_step)) continue;
       const uint32_t b = seg_bytes(seg0, seg_step, i);
       if constexpr (DELTA)
-        store_stream<ATTNRES_NT_STORE_CUR>(at(p.prefix + t * p.prefix_stride, b), x[NB][i]);
+        store_row<ATTNRES_NT_STORE_CUR>(p, p.prefix + t * p.prefix_stride, b, x[NB][i]);
       if (p.widx >= 0)
-        store_stream<ATTNRES_NT_STORE_CUR>(
-            at(p.blocks + t * p.tok_stride + p.widx * p.slot_stride, b), x[NB][i]);
+        store_row<ATTNRES_NT_STORE_CUR>(p, p.blocks + t * p.tok_stride + p.widx * p.slot_stride,
+                                        b, x[NB][i]);
     }
   }
 
@@ -697,7 +714,6 @@ struct Token {
     if constexpr (!CUR_DONE) store_cur(p, t, seg0, seg_step);
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
-      if (!in_row(p, seg0 + i * seg_step)) continue;
       u32x4 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -707,7 +723,7 @@ struct Token {
         else
           o[k] = pack_bf16x2(y[i][2 * k], y[i][2 * k + 1]);
       }
-      store_stream(at(p.out + t * p.out_stride, seg_bytes(seg0, seg_step, i)), o);
+      store_row<ATTNRES_NT_STORES>(p, p.out + t * p.out_stride, seg_bytes(seg0, seg_step, i), o);
     }
   }
 };
@@ -960,11 +976,15 @@ __device__ __forceinline__ float sum_row_partials_n(const float *v, int n4) {
 // LR > 0 (kAnyLdsRows bank rows staged in LDS, launched with LR * SPL *
 // blockDim.x * 16 bytes of dynamic LDS): the same steps with those rows held
 // in LDS instead of registers, for one more resident workgroup per CU where
-// the registers are what limits it (see anyh_lds_rows).
-template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, int LR = 0>
+// the registers are what limits it (see anyh_lds_rows).  Register budgets
+// for that: four segments per lane, 168 VGPRs (two workgroups of 5-6 waves);
+// two segments, 96 for four 5-wave workgroups, or with W6 80 for four 6-wave
+// ones (six waves per SIMD).
+template <int SPL, bool MASKED, int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, int LR = 0,
+          bool W6 = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWave, kAnyMaxThreads),
                                amdgpu_waves_per_eu(LR == 0 ? (SPL <= 2 ? 4 : 2)
-                                                           : (SPL <= 2 ? 5 : 3))))
+                                                           : (SPL <= 2 ? (W6 ? 6 : 5) : 3))))
 attnres_anyh_kernel(KParams p) {
   constexpr int NS = NB + 1;
   constexpr bool STG = LR > 0;
@@ -1649,30 +1669,36 @@ KernelFn anyh_fn(bool d, bool o, bool cache_rw) {
 // The any-H kernel with kAnyLdsRows bank rows staged into LDS (4..8 bank
 // rows, two or four segments per lane).
 constexpr int kAnyLdsRows = 3;
-template <int SPL, bool MASKED, int NB>
+template <int SPL, bool MASKED, int NB, bool W6>
 KernelFn anyh_lds_fn(bool d, bool o, bool c) {
   if constexpr (NB >= 4) {
     constexpr int L = kAnyLdsRows;
     if (c) {
       if (d)
-        return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, true, L>
-                 : attnres_anyh_kernel<SPL, MASKED, NB, true, false, true, L>;
-      return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, true, L>
-               : attnres_anyh_kernel<SPL, MASKED, NB, false, false, true, L>;
+        return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, true, L, W6>
+                 : attnres_anyh_kernel<SPL, MASKED, NB, true, false, true, L, W6>;
+      return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, true, L, W6>
+               : attnres_anyh_kernel<SPL, MASKED, NB, false, false, true, L, W6>;
     }
     if (d)
-      return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, false, L>
-               : attnres_anyh_kernel<SPL, MASKED, NB, true, false, false, L>;
-    return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, false, L>
-             : attnres_anyh_kernel<SPL, MASKED, NB, false, false, false, L>;
+      return o ? attnres_anyh_kernel<SPL, MASKED, NB, true, true, false, L, W6>
+               : attnres_anyh_kernel<SPL, MASKED, NB, true, false, false, L, W6>;
+    return o ? attnres_anyh_kernel<SPL, MASKED, NB, false, true, false, L, W6>
+             : attnres_anyh_kernel<SPL, MASKED, NB, false, false, false, L, W6>;
   }
   return nullptr;
 }
 template <int NB>
 KernelFn anyh_lds_pick(const AnyShape &sh, bool d, bool o, bool c) {
-  if (sh.spl == 2)
-    return sh.masked ? anyh_lds_fn<2, true, NB>(d, o, c) : anyh_lds_fn<2, false, NB>(d, o, c);
-  return sh.masked ? anyh_lds_fn<4, true, NB>(d, o, c) : anyh_lds_fn<4, false, NB>(d, o, c);
+  if (sh.spl == 2) {
+    if (sh.threads / kWave >= 6)
+      return sh.masked ? anyh_lds_fn<2, true, NB, true>(d, o, c)
+                       : anyh_lds_fn<2, false, NB, true>(d, o, c);
+    return sh.masked ? anyh_lds_fn<2, true, NB, false>(d, o, c)
+                     : anyh_lds_fn<2, false, NB, false>(d, o, c);
+  }
+  return sh.masked ? anyh_lds_fn<4, true, NB, false>(d, o, c)
+                   : anyh_lds_fn<4, false, NB, false>(d, o, c);
 }
 KernelFn pick_anyh_lds(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw) {
   switch (nb) {
@@ -1691,20 +1717,18 @@ KernelFn pick_anyh_lds(const AnyShape &sh, int nb, bool d, bool o, bool cache_rw
 // second round of loads per token (the rows after the staged ones wait for
 // registers).
 // - Two segments per lane: the plain kernel may take 128 VGPRs (four waves
-//   per SIMD), so three 5-wave workgroups fit (H = 4104..5120), and a call of
-//   more tokens than that runs a partial second round (T = 1024 at H = 5120:
-//   768 + 256).  Staged, the kernel is built for 96 VGPRs and four fit, with
-//   30 KB of LDS each.  Measured (T = 1024, delta and norm, µs per call,
-//   plain / LDS-direct rows / staged): H = 5120 nb = 8 28.6 / 24.8 / 23.6,
-//   nb = 4 19.9 / 18.6 / 18.9; H = 4104 nb = 8 - / 22.8 / 21.7; T = 2048
-//   H = 4608 - / 45.1 / 42.5.  With a sixth wave (two plain workgroups per
-//   CU, three staged), plain / staged: H = 5632 (masked) T = 600 18.3 /
-//   18.6, T = 1024 30.7 / 26.1, T = 2048 53.2 / 50.7; H = 6144 T = 600 19.1 /
-//   22.2, T = 1024 32.1 / 33.5, T = 2048 55.7 / 55.4 (yet nb = 4 24.0 / 21.2).
-//   Staging lost where a row is a whole number of 4 KB (H = 6144, 10240,
-//   12288), perhaps from how the rows fall on the memory channels (not
-//   measured), and won elsewhere.  So 5-wave workgroups, and 6-wave ones
-//   over masked rows, for more tokens than three per CU.
+//   per SIMD), so three 5-wave workgroups fit (H = 4104..5120) or two 6-wave
+//   ones (H = 5128..6144), and a call of more tokens than that runs a partial
+//   second round (T = 1024 at H = 5120: 768 + 256).  Staged, four fit: the
+//   5-wave kernels are built for 96 VGPRs (30 KB of LDS each), the 6-wave
+//   ones for 80 (six waves per SIMD; 37 KB of LDS each, 157 KB per CU).
+//   Measured (T = 1024, delta and norm, µs per call, plain / LDS-direct rows
+//   / staged): H = 5120 nb = 8 28.6 / 24.8 / 23.6, nb = 4 19.9 / 18.6 /
+//   18.8; H = 4104 - / 22.8 / 20.9; H = 4608 T = 2048 - / 45.1 / 42.5; 6
+//   waves, plain / staged: H = 5632 30.8 / 26.3, H = 6144 32.2 / 28.7 (nb = 4
+//   24.1 / 21.2), T = 2048 56.0 / 54.3, T = 600 19.1 / 19.8.  So 5- and
+//   6-wave workgroups, for more tokens than three per CU.  (The 6-wave
+//   kernels at 96 VGPRs fitted three per CU, not four, and then lost.)
 // - Four segments per lane: a token of 5-6 waves (H = 8200..12288) fills a
 //   CU's registers (200+ VGPRs), one workgroup per CU; staged it takes at
 //   most 168 (three waves per SIMD), so two fit, with 61-74 KB of LDS each.
@@ -1720,7 +1744,7 @@ bool anyh_lds_rows(const AnyShape &sh, int64_t T, int nb, int cus, size_t *dyn) 
   if (!ATTNRES_ANYH_STAGED || nb < 4) return false;
   bool use;
   if (sh.spl == 2)
-    use = (waves == 5 || (waves == 6 && sh.masked)) && T > int64_t(3) * cus;
+    use = (waves == 5 || waves == 6) && T > int64_t(3) * cus;
   else
     use = T > int64_t(cus) && (waves == 5 || (waves == 6 && T <= int64_t(2) * cus));
   if (!use) return false;
@@ -2007,8 +2031,9 @@ int allow_dynamic_lds(KernelFn fn, size_t bytes) {
 // such workgroup (384 lanes, four segments) takes 72 KB.
 constexpr size_t kAnyLdsMaxBytes = size_t(kAnyLdsRows) * 4 * 384 * 16;
 int allow_staged_lds() {
-  const AnyShape shapes[4] = {
-      {2, 5 * kWave, false}, {2, 5 * kWave, true}, {4, 6 * kWave, false}, {4, 6 * kWave, true}};
+  const AnyShape shapes[6] = {{2, 5 * kWave, false}, {2, 5 * kWave, true},
+                              {2, 6 * kWave, false}, {2, 6 * kWave, true},
+                              {4, 6 * kWave, false}, {4, 6 * kWave, true}};
   for (const AnyShape &sh : shapes)
     for (int nb = 4; nb <= kMaxBlocks; ++nb)
       for (int f = 0; f < 8; ++f) {

@@ -158,11 +158,13 @@ def test_long_prefill_full(G, T):
 
 
 # The any-H kernel with three bank rows staged in LDS, two segments per lane:
-# 5-wave workgroups (H 4104..5120) and 6-wave ones over masked rows (H
-# 5128..6136), 4..8 bank rows, more tokens than three per compute unit (T >
-# 768 on 256 CUs); masked rows, and the cached-read form (T * H >= 1024 * 7168
-# with a delta and a written source slot).
+# 5-wave workgroups (H 4104..5120) and 6-wave ones (H 5128..6144), 4..8 bank
+# rows, more tokens than three per compute unit (T > 768 on 256 CUs); masked
+# rows, and the cached-read form (T * H >= 1024 * 7168 with a delta and a
+# written source slot).
 LDS_ROW_CASES = [
+    dict(H=6144, T=1024, nb=8, widx=3),                          # 6 waves
+    dict(H=6144, T=1300, nb=4, has_onorm=False, widx=1),         # 6 waves, cached
     dict(H=5632, T=1024, nb=8, widx=3),                          # 6 waves, masked
     dict(H=5128, T=800, nb=5, has_delta=False, widx=4),         # 6 waves, one segment over
     dict(H=6136, T=1300, nb=8, widx=7, recipe="soft"),           # 6 waves, masked and cached
