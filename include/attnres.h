@@ -293,6 +293,13 @@ const char *attnres_strerror(int status);
 /* The hipError_t of the last failed HIP call in this library (0 if none). */
 int attnres_last_hip_error(void);
 
+/* For tests of the failure path only.  While enabled (enable != 0), every
+ * split-path call of this process waits for a generation of the exchanged
+ * words that never comes, gives up after 64 polls and raises the device flag
+ * that attnres_device_status reports; the results of those calls are not
+ * valid.  Every kernel still exits.  Disabled by default; returns ATTNRES_OK. */
+int attnres_debug_force_wait_failure(int enable);
+
 /* The kernel attnres_fwd (ATTNRES_PATH_AUTO) runs for a call of T tokens,
  * hidden size H and num_blocks block rows: ATTNRES_PATH_ROW (the tuned row
  * kernel, H = 7168), ATTNRES_PATH_SPLIT or ATTNRES_PATH_ANY_H; or

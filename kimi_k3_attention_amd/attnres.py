@@ -82,6 +82,8 @@ _lib.attnres_last_hip_error.argtypes = []
 _lib.attnres_last_hip_error.restype = _int
 _lib.attnres_auto_path.argtypes = [_i64, _i64, _int]
 _lib.attnres_auto_path.restype = _int
+_lib.attnres_debug_force_wait_failure.argtypes = [_int]
+_lib.attnres_debug_force_wait_failure.restype = _int
 
 
 def lib() -> ctypes.CDLL:
@@ -329,3 +331,9 @@ def attnres_auto_path(T: int, H: int, num_blocks: int) -> int:
     if rc < 0:
         raise AttnResError(rc, "attnres_auto_path")
     return rc
+
+
+def attnres_debug_force_wait_failure(enable: bool) -> None:
+    """Tests of the failure path only: while enabled, split-path calls give
+    up their cross-workgroup waits (see include/attnres.h)."""
+    _lib.attnres_debug_force_wait_failure(1 if enable else 0)

@@ -154,6 +154,8 @@ struct KParams {
   float inv_h;            // 1 / H
   uint64_t *ws_part;       // split path: tagged words, 14 parts per token
   unsigned *ws_flag;
+  int spin_limit;          // split path: polls before a wait gives up
+  uint32_t wait_skew;      // split path: added to the awaited generation (0; tests only)
   float *partial;          // two-kernel form: the bank part's state (see attnres_bank_kernel)
 };
 
@@ -1289,9 +1291,10 @@ __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return uint32_t(w >> 32
 __device__ __forceinline__ float value_of(uint64_t w) { return __uint_as_float(uint32_t(w)); }
 
 // Sums word `idx` over the kParts parts (fixed order), once every part has
-// written it with generation `gen`.
+// written it with generation `gen`; after `spin_limit` polls it gives up and
+// raises the device flag (the sum is then not valid).
 __device__ __forceinline__ float gather(const uint64_t *tok_ws, int idx, uint32_t gen,
-                                        unsigned *flag) {
+                                        unsigned *flag, int spin_limit) {
   uint64_t w[kParts];
   for (int spins = 0;; ++spins) {
     bool ready = true;
@@ -1300,7 +1303,7 @@ __device__ __forceinline__ float gather(const uint64_t *tok_ws, int idx, uint32_
 #pragma unroll
     for (int r = 0; r < kParts; ++r) ready = ready && tag_of(w[r]) == gen;
     if (ready) break;
-    if (spins >= kSpinLimit) {
+    if (spins >= spin_limit) {
       __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
@@ -1424,7 +1427,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
       const float s = wave_sum_lane63(sum_sq<SPL>(y));
       if (lane == kWave - 1) tagged_store(slot, s, gen0);
       float total = 0.f;
-      if (lane == 0) total = gather(tok_ws, 0, gen0, p.ws_flag);
+      if (lane == 0) total = gather(tok_ws, 0, gen0 + p.wait_skew, p.ws_flag, p.spin_limit);
       rsig = rsqrtf(lane_value(total, 0) * inv_h + p.out_eps);
     }
     tk.store(p, t, seg0, seg_step, y, rsig);
@@ -1579,7 +1582,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
 
   tk.issue_onw(p, seg0, seg_step);
   // The token's totals: lane v holds word v summed over the parts.
-  const float total = lane < NV ? gather(tok_ws, lane, gen, p.ws_flag) : 0.f;
+  const float total = lane < NV ? gather(tok_ws, lane, gen + p.wait_skew, p.ws_flag, p.spin_limit) : 0.f;
   float ss_j;
   const float p_lane = weights_from_totals<NS, ONORM>(total, p.rms_eps, inv_h, ss_j);
   float y[SPL][8];
@@ -1595,7 +1598,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
       // Every part sees the same totals and takes the same branch.
       const float sy = wave_sum_lane63(sum_sq<SPL>(y));
       if (lane == kWave - 1) tagged_store(slot + kSlotYsq, sy, gen);
-      tot = gather(tok_ws, kSlotYsq, gen, p.ws_flag);
+      tot = gather(tok_ws, kSlotYsq, gen + p.wait_skew, p.ws_flag, p.spin_limit);
     }
     rsig = rsqrtf(tot * inv_h + p.out_eps);
   }
@@ -1909,6 +1912,8 @@ struct DeviceWorkspace {
 DeviceWorkspace g_ws[kMaxDevices];
 std::mutex g_ws_mu;
 std::atomic<int> g_last_hip{0};
+std::atomic<bool> g_force_wait_failure{false};  // attnres_debug_force_wait_failure
+constexpr int kForcedSpinLimit = 64;
 
 }  // namespace
 
@@ -2095,6 +2100,11 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
   kp.out_eps = a.output_norm_weight ? a.output_norm_eps : 0.f;
   kp.widx = a.block_write_idx;
   kp.T = int(a.T);
+  // A test of the failure path may have the split path's waits look for a
+  // generation that never comes, and give up after a few polls.
+  const bool force_fail = g_force_wait_failure.load();
+  kp.spin_limit = force_fail ? kForcedSpinLimit : kSpinLimit;
+  kp.wait_skew = force_fail ? 0x40000000u : 0u;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   int dev = 0;
@@ -2422,6 +2432,11 @@ extern "C" int attnres_device_status(int device) {
 }
 
 extern "C" int attnres_last_hip_error(void) { return g_last_hip.load(); }
+
+extern "C" int attnres_debug_force_wait_failure(int enable) {
+  g_force_wait_failure.store(enable != 0);
+  return ATTNRES_OK;
+}
 
 extern "C" int attnres_auto_path(int64_t T, int64_t H, int num_blocks) {
   using namespace attnres;
