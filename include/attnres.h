@@ -35,7 +35,9 @@
  *
  * Tensors are bf16 (passed as raw 16-bit patterns) in device memory.  The
  * library keeps no pointer after a call returns; the caller owns every buffer
- * and keeps it alive until the stream work completes.  Arithmetic is fp32.
+ * and keeps it alive until the stream work completes.  Arithmetic is fp32:
+ * inputs must be finite, and a row's sum of squares must stay within fp32's
+ * range (at H = 7168, an RMS below about 2e17), or it overflows.
  *
  * Errors: every entry point returns ATTNRES_OK (0) or a negative code.  All
  * argument checks run on the host before any GPU work, so a rejected call
