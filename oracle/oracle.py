@@ -106,6 +106,12 @@ def attnres_oracle(prefix: np.ndarray, delta: Optional[np.ndarray],
     prefix = np.ascontiguousarray(prefix, dtype=np.uint16)
     T, H = prefix.shape
     nsrc = num_blocks + 1
+    if T > 0 and (num_blocks > 0 or block_write_idx >= 0):
+        # The C code trusts the strides: refuse a bank buffer they overrun.
+        need = (T - 1) * int(token_stride) + (int(cap) - 1) * int(slot_stride) + H
+        if bank is None or np.asarray(bank).size < need:
+            raise ValueError(f"bank holds {0 if bank is None else np.asarray(bank).size} "
+                             f"elements; the strides address {need}")
     pre = prefix.copy()
     bnk = None if bank is None else np.array(bank, dtype=np.uint16, copy=True)
     dlt = None if delta is None else np.ascontiguousarray(delta, dtype=np.uint16)

@@ -121,6 +121,12 @@ def oracle_full_threaded(inp: W.Inputs, threads: int = 16):
     import oracle
     c = inp.case
     T, ts = c.T, c.token_stride
+    if c.cap > 1 and (c.cap - 1) * c.slot_stride + c.H > ts:
+        # A token's rows do not lie within its token stride (a slot-major
+        # bank): token ranges have no bank slice of their own, so run the
+        # oracle over the whole call at once.
+        r = oracle_full(inp)
+        return FullRef(r.out_bits, r.prefix_after, r.bank_after)
     n = max(1, min(threads, T))
     bounds = [(T * k // n, T * (k + 1) // n) for k in range(n)]
     bank_after = inp.bank.copy()

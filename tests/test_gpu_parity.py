@@ -163,6 +163,8 @@ def test_long_prefill_full(G, T):
 # rows, and the cached-read form (T * H >= 1024 * 7168 with a delta and a
 # written source slot).
 LDS_ROW_CASES = [
+    dict(H=5120, T=900, nb=8, widx=3, slot_major=True),          # slot-major bank
+    dict(H=5632, T=800, nb=6, widx=5, row_pad=40, cap=7),        # strided rows, 6 waves
     dict(H=6144, T=1024, nb=8, widx=3),                          # 6 waves
     dict(H=6144, T=1300, nb=4, has_onorm=False, widx=1),         # 6 waves, cached
     dict(H=5632, T=1024, nb=8, widx=3),                          # 6 waves, masked
@@ -196,6 +198,7 @@ def test_any_h_rows_in_lds(G, kw):
 # and the cached-read form (T * H >= 1024 * 7168 with a delta and a written
 # slot).
 STAGED_CASES = [
+    dict(H=9216, T=300, nb=8, widx=2, slot_major=True, row_pad=24),  # slot-major, strided
     dict(H=10240, T=800, nb=8, widx=3),                          # cached rewritten rows
     dict(H=12288, T=300, nb=4, has_onorm=False, widx=-1),       # 6 waves
     dict(H=10240, T=400, nb=6, has_delta=False, widx=5),
