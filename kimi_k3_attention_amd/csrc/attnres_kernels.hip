@@ -1270,12 +1270,15 @@ static_assert(3 * kParts * kPartThreads * kSeg >= kMaxHidden,
 // split path: kParts single-wave workgroups per token
 // ---------------------------------------------------------------------------
 
-// The exchange between the kParts workgroups of a token crosses XCDs, whose
-// L2 caches are not coherent with each other.  Every exchanged value is a
-// self-validating 64-bit word, (generation << 32) | float bits, written and
-// read with single device-coherent (agent-scope atomic) accesses, which bypass
-// the non-coherent L2: no L2 writeback or invalidate, no counter, and a reader
-// needs one round trip once the words are there.  A part's generation for this
+// The kParts workgroups of a token are placed on one XCD (see the kernel),
+// but nothing in the launch guarantees that placement, and the L2 caches of
+// different XCDs are not coherent with each other.  So every exchanged value
+// is a self-validating 64-bit word, (generation << 32) | float bits, written
+// and read with single device-coherent (agent-scope atomic) accesses, which
+// bypass the non-coherent L2: no L2 writeback or invalidate, no counter, and
+// a reader needs one round trip once the words are there.  (A load with only
+// the workgroup-scope bit would be served from the reading CU's own L1 and
+// never see a partner's store.)  A part's generation for this
 // call is its own word 0's generation plus one: every call rewrites word 0 of
 // all kParts parts of a token with the same generation, so the parts agree
 // without communicating (the workspace starts at zero).  Waits are bounded; a
