@@ -180,7 +180,8 @@ int attnres_fwd_strided(void *prefix, int64_t prefix_stride,
  * split path's (its cross-workgroup exchange words and fault flag).  This
  * entry point gives it a static device array of 1,835,264 bytes per device
  * (ATTNRES_SPLIT_MAX_TOKENS tokens), held until the process ends, instead of
- * the allocated workspace.  A split-path call of more than
+ * the allocated workspace (one frame: without the allocated workspace's
+ * choice of the frame nearer each XCD).  A split-path call of more than
  * ATTNRES_SPLIT_MAX_TOKENS tokens is rejected with ATTNRES_E_UNSUPPORTED
  * before any GPU work.  The array's device address is taken, and the array
  * cleared, once per device: in attnres_init(device), or else at the first
@@ -272,9 +273,15 @@ int attnres_validate_strided(const void *prefix, int64_t prefix_stride,
                              int block_write_idx, const void *out, int64_t out_stride,
                              int64_t T, int64_t H);
 
-/* Allocates and clears the split path's workspace on `device` (about 1.8 MB:
- * tagged partial-sum words and a fault flag), and takes the address of (and
- * clears) attnres_fwd_noalloc's static array there.  It also lets the any-H
+/* Allocates and clears the split path's workspace on `device`: tagged
+ * partial-sum words and a fault flag, in two 2 MB frames (4 MB).  It tries
+ * four 2 MB allocations, times a device-scope store and load to each from
+ * every XCD with one short kernel (64 single-wave workgroups, synchronous),
+ * keeps the pair that best serves all XCDs and frees the other two: a store
+ * to a frame homed on the writer's half of the chip is acknowledged about
+ * twice as fast, and the split path's workgroups write and poll the nearer
+ * frame (reading both if their partners' words are not there).  It also takes the address of (and clears)
+ * attnres_fwd_noalloc's static array there.  It also lets the any-H
  * kernels that stage bank rows in LDS (H = 8200..12288) take their 61-72 KB of
  * dynamic LDS, which a call would otherwise set up at its first use.
  * Idempotent.  Call it outside stream capture. */
@@ -301,6 +308,16 @@ int attnres_last_hip_error(void);
  * that attnres_device_status reports; the results of those calls are not
  * valid.  Every kernel still exits.  Disabled by default; returns ATTNRES_OK. */
 int attnres_debug_force_wait_failure(int enable);
+
+/* For tests only.  Which of the split path's two workspace frames each
+ * workgroup writes.  A workgroup polls the frame it writes and, after 16
+ * polls, both, so the choice may change speed but not results: mode -1 (the
+ * default) follows the set-up timing by the workgroup's XCD; 0..255 is a
+ * mask with one bit per XCD (set: frame B); 256 writes frame B from the odd
+ * parts of a token and frame A from the even ones.
+ * Affects calls made after it, in this process.  Returns ATTNRES_OK, or
+ * ATTNRES_E_SHAPE for another mode. */
+int attnres_debug_workspace_frames(int mode);
 
 /* The kernel attnres_fwd (ATTNRES_PATH_AUTO) runs for a call of T tokens,
  * hidden size H and num_blocks block rows: ATTNRES_PATH_ROW (the tuned row

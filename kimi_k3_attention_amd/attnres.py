@@ -84,6 +84,8 @@ _lib.attnres_auto_path.argtypes = [_i64, _i64, _int]
 _lib.attnres_auto_path.restype = _int
 _lib.attnres_debug_force_wait_failure.argtypes = [_int]
 _lib.attnres_debug_force_wait_failure.restype = _int
+_lib.attnres_debug_workspace_frames.argtypes = [_int]
+_lib.attnres_debug_workspace_frames.restype = _int
 
 
 def lib() -> ctypes.CDLL:
@@ -337,3 +339,12 @@ def attnres_debug_force_wait_failure(enable: bool) -> None:
     """Tests of the failure path only: while enabled, split-path calls give
     up their cross-workgroup waits (see include/attnres.h)."""
     _lib.attnres_debug_force_wait_failure(1 if enable else 0)
+
+
+def attnres_debug_workspace_frames(mode: int) -> None:
+    """Tests only: which of the split path's two workspace frames each
+    workgroup writes (-1 default, 0..255 a mask by XCD, 256 by part parity;
+    see include/attnres.h)."""
+    rc = _lib.attnres_debug_workspace_frames(int(mode))
+    if rc != ATTNRES_OK:
+        raise AttnResError(rc, "attnres_debug_workspace_frames")

@@ -44,7 +44,9 @@
 // delta and out are runtime values.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cstdint>
 #include <mutex>
 
@@ -152,7 +154,10 @@ struct KParams {
   int threads;            // lanes per workgroup of the any-H launch shape (a kernel
                           // argument: blockDim.x would be read with a vector load)
   float inv_h;            // 1 / H
-  uint64_t *ws_part;       // split path: tagged words, 14 parts per token
+  uint64_t *ws_part;       // split path: tagged words, 14 parts per token (frame A)
+  uint64_t *ws_part_b;     // the same words in frame B (== ws_part: one frame)
+  unsigned ws_near;        // bit x: frame B is the one a part on XCD x writes
+  int ws_by_part;          // tests only: bit `part` of ws_near chooses instead
   unsigned *ws_flag;
   int spin_limit;          // split path: polls before a wait gives up
   uint32_t wait_skew;      // split path: added to the awaited generation (0; tests only)
@@ -1293,16 +1298,43 @@ __device__ __forceinline__ void tagged_store(uint64_t *w, float v, uint32_t gen)
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return uint32_t(w >> 32); }
 __device__ __forceinline__ float value_of(uint64_t w) { return __uint_as_float(uint32_t(w)); }
 
+// The later of two generations (they count calls, modulo 2^32).
+__device__ __forceinline__ uint32_t later_gen(uint32_t a, uint32_t b) {
+  return int32_t(a - b) > 0 ? a : b;
+}
+
+// Two memory frames hold a copy each of the split path's words.  A device-
+// scope store is acknowledged about twice as fast when its 2 MB frame is homed
+// on the writing XCD's half of the chip (about 220 against 460 ns on MI355X),
+// and a part's first poll waits for its own store's acknowledgement (loads and
+// stores retire in order); a poll of the far frame costs a far round trip too.
+// So a part writes its words to the frame that the host found nearer its XCD
+// and polls that frame, where a token's parts (all on one XCD) put theirs;
+// after kNearPolls polls it reads both frames.  Where the parts of a token run
+// decides only speed, never what is read.
+constexpr int kNearPolls = 16;
+__device__ __forceinline__ unsigned hw_xcc_id() {
+  return __builtin_amdgcn_s_getreg(20 | (3 << 11)) & 7u;  // HW_REG_XCC_ID, 4 bits
+}
+
 // Sums word `idx` over the kParts parts (fixed order), once every part has
-// written it with generation `gen`; after `spin_limit` polls it gives up and
-// raises the device flag (the sum is then not valid).
-__device__ __forceinline__ float gather(const uint64_t *tok_ws, int idx, uint32_t gen,
-                                        unsigned *flag, int spin_limit) {
+// written it with generation `gen` into either frame (the near one is polled
+// first); after `spin_limit` polls it gives up and raises the device flag
+// (the sum is then not valid).
+__device__ __forceinline__ float gather(const uint64_t *tok_near, const uint64_t *tok_far,
+                                        int idx, uint32_t gen, unsigned *flag, int spin_limit) {
   uint64_t w[kParts];
   for (int spins = 0;; ++spins) {
     bool ready = true;
 #pragma unroll
-    for (int r = 0; r < kParts; ++r) w[r] = tagged_load(tok_ws + r * kSlot + idx);
+    for (int r = 0; r < kParts; ++r) w[r] = tagged_load(tok_near + r * kSlot + idx);
+    if (spins >= kNearPolls) {
+      uint64_t wf[kParts];
+#pragma unroll
+      for (int r = 0; r < kParts; ++r) wf[r] = tagged_load(tok_far + r * kSlot + idx);
+#pragma unroll
+      for (int r = 0; r < kParts; ++r) w[r] = tag_of(w[r]) == gen ? w[r] : wf[r];
+    }
 #pragma unroll
     for (int r = 0; r < kParts; ++r) ready = ready && tag_of(w[r]) == gen;
     if (ready) break;
@@ -1409,8 +1441,15 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   const int seg0 = part * kPartThreads * SPL + lane;
   constexpr int seg_step = kPartThreads;
   const float inv_h = SPL == 1 && !MASKED ? kInvHidden : p.inv_h;
-  uint64_t *const tok_ws = p.ws_part + size_t(t) * kParts * kSlot;
-  uint64_t *const slot = tok_ws + part * kSlot;
+  // The token's words in frames A and B; this part writes `slot`, in the
+  // frame nearer its XCD, and reads both.  Its own word 0 holds the last
+  // call's generation in one of the two frames.
+  uint64_t *const tok_a = p.ws_part + size_t(t) * kParts * kSlot;
+  uint64_t *const tok_b = p.ws_part_b + size_t(t) * kParts * kSlot;
+  const unsigned near_b = (p.ws_near >> (p.ws_by_part ? unsigned(part) : hw_xcc_id())) & 1u;
+  uint64_t *const tok_near = near_b ? tok_b : tok_a;
+  uint64_t *const tok_far = near_b ? tok_a : tok_b;
+  uint64_t *const slot = tok_near + part * kSlot;
 
   if constexpr (NB == 0) {
     // One source, weight exactly 1: y = cur.  Only an output norm needs the
@@ -1418,7 +1457,9 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
     // (so every such call still rewrites word 0 of all parts).  Without a
     // norm nothing is exchanged.
     uint32_t gen0 = 0;
-    if constexpr (ONORM) gen0 = tag_of(tagged_load(slot)) + 1u;
+    if constexpr (ONORM)
+      gen0 = later_gen(tag_of(tagged_load(tok_a + part * kSlot)),
+                       tag_of(tagged_load(tok_b + part * kSlot))) + 1u;
     Token<NB, DELTA, ONORM, SPL, MASKED> tk;
     tk.issue(p, t, seg0, seg_step);
     tk.finish_cur();
@@ -1430,7 +1471,8 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
       const float s = wave_sum_lane63(sum_sq<SPL>(y));
       if (lane == kWave - 1) tagged_store(slot, s, gen0);
       float total = 0.f;
-      if (lane == 0) total = gather(tok_ws, 0, gen0 + p.wait_skew, p.ws_flag, p.spin_limit);
+      if (lane == 0)
+        total = gather(tok_near, tok_far, 0, gen0 + p.wait_skew, p.ws_flag, p.spin_limit);
       rsig = rsqrtf(lane_value(total, 0) * inv_h + p.out_eps);
     }
     tk.store(p, t, seg0, seg_step, y, rsig);
@@ -1438,7 +1480,8 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   }
 
   // This call's generation (issued first; used only when publishing).
-  const uint32_t gen = tag_of(tagged_load(slot)) + 1u;
+  const uint32_t gen = later_gen(tag_of(tagged_load(tok_a + part * kSlot)),
+                                 tag_of(tagged_load(tok_b + part * kSlot))) + 1u;
 
   Token<NB, DELTA, ONORM, SPL, MASKED> tk;
   tk.issue(p, t, seg0, seg_step);
@@ -1585,7 +1628,9 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
 
   tk.issue_onw(p, seg0, seg_step);
   // The token's totals: lane v holds word v summed over the parts.
-  const float total = lane < NV ? gather(tok_ws, lane, gen + p.wait_skew, p.ws_flag, p.spin_limit) : 0.f;
+  const float total =
+      lane < NV ? gather(tok_near, tok_far, lane, gen + p.wait_skew, p.ws_flag, p.spin_limit)
+                : 0.f;
   float ss_j;
   const float p_lane = weights_from_totals<NS, ONORM>(total, p.rms_eps, inv_h, ss_j);
   float y[SPL][8];
@@ -1601,11 +1646,45 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
       // Every part sees the same totals and takes the same branch.
       const float sy = wave_sum_lane63(sum_sq<SPL>(y));
       if (lane == kWave - 1) tagged_store(slot + kSlotYsq, sy, gen);
-      tot = gather(tok_ws, kSlotYsq, gen + p.wait_skew, p.ws_flag, p.spin_limit);
+      tot = gather(tok_near, tok_far, kSlotYsq, gen + p.wait_skew, p.ws_flag, p.spin_limit);
     }
     rsig = rsqrtf(tot * inv_h + p.out_eps);
   }
   tk.store(p, t, seg0, seg_step, y, rsig);
+}
+
+// ---------------------------------------------------------------------------
+// workspace frames: which one is nearer each XCD
+// ---------------------------------------------------------------------------
+
+constexpr int kFrameCandidates = 4;  // 2 MB allocations timed at set-up
+constexpr int kCalibWgs = 64;        // eight per XCD
+constexpr int kCalibRounds = 8;
+
+struct CalibArgs {
+  uint64_t *lines[kFrameCandidates];  // a spare area of each candidate frame
+  int *out;                           // per workgroup: its XCD, then ticks per candidate
+  int candidates;
+};
+
+// Lane 0 of each workgroup times kCalibRounds device-scope store-then-load
+// round trips to its own 128-byte line of every candidate frame: the load
+// retires after the store's acknowledgement, which is what a publishing part
+// of the split path waits for.  Every wait is bounded.
+__global__ void __launch_bounds__(kWave) attnres_frame_calibration_kernel(CalibArgs a) {
+  if (threadIdx.x != 0) return;
+  int *const o = a.out + blockIdx.x * (1 + kFrameCandidates);
+  o[0] = int(hw_xcc_id());
+  for (int c = 0; c < a.candidates; ++c) {
+    uint64_t *const w = a.lines[c] + blockIdx.x * 16;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (int k = 1; k <= kCalibRounds; ++k) {
+      __hip_atomic_store(w, uint64_t(k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int s = 0; s < 1000; ++s)
+        if (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == uint64_t(k)) break;
+    }
+    o[1 + c] = int(__builtin_amdgcn_s_memrealtime() - t0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1897,6 +1976,14 @@ constexpr int kMaxDevices = 64;
 constexpr size_t kPartBytes = size_t(ATTNRES_SPLIT_MAX_TOKENS) * kParts * kSlot * sizeof(uint64_t);
 constexpr size_t kFlagBytes = 256;
 constexpr size_t kWorkspaceBytes = kPartBytes + kFlagBytes;
+// The allocated workspace is two 2 MB frames (A holds the fault flag too);
+// the calibration uses their last 16 KB.
+constexpr size_t kFrameBytes = size_t(2) << 20;
+constexpr size_t kCalibLines = kFrameBytes - 16384;
+constexpr size_t kCalibOut = kFrameBytes - 4096;
+static_assert(kWorkspaceBytes <= kCalibLines, "split workspace overlaps the calibration area");
+static_assert(size_t(kCalibWgs) * 128 <= kCalibOut - kCalibLines, "calibration lines");
+static_assert(size_t(kCalibWgs) * (1 + kFrameCandidates) * sizeof(int) <= 4096, "calibration out");
 
 // Split calls on one device must run one after another: they share the
 // workspace, and two split kernels running at once could each hold the
@@ -1904,8 +1991,11 @@ constexpr size_t kWorkspaceBytes = kPartBytes + kFlagBytes;
 // different stream than the previous one therefore makes its stream wait for
 // everything enqueued on the previous stream so far (outside graph capture).
 struct DeviceWorkspace {
-  void *base = nullptr;
+  void *base = nullptr;           // frame A: the parts' words, then the fault flag
+  void *base_b = nullptr;         // frame B: the parts' words
   uint64_t *part = nullptr;
+  uint64_t *part_b = nullptr;
+  unsigned near = 0;              // bit x: a part on XCD x writes frame B
   unsigned *flag = nullptr;
   hipEvent_t handoff = nullptr;   // recorded on the previous stream at a switch
   hipStream_t last_stream = nullptr;
@@ -1916,6 +2006,7 @@ DeviceWorkspace g_ws[kMaxDevices];
 std::mutex g_ws_mu;
 std::atomic<int> g_last_hip{0};
 std::atomic<bool> g_force_wait_failure{false};  // attnres_debug_force_wait_failure
+std::atomic<int> g_frames_mode{-1};               // attnres_debug_workspace_frames
 constexpr int kForcedSpinLimit = 64;
 
 }  // namespace
@@ -1945,28 +2036,85 @@ int hip_fail(hipError_t e) {
   return ATTNRES_E_HIP;
 }
 
+// Times a device-scope store and load from every XCD to each candidate frame
+// (the calibration kernel); ticks[x][c] is the fastest workgroup on XCD x,
+// and an XCD that ran none (a partition with fewer) counts the same for all.
+hipError_t calibrate_frames(void *const (&cand)[kFrameCandidates],
+                            int (&ticks)[8][kFrameCandidates]) {
+  CalibArgs a{};
+  for (int c = 0; c < kFrameCandidates; ++c)
+    a.lines[c] = reinterpret_cast<uint64_t *>(static_cast<char *>(cand[c]) + kCalibLines);
+  a.out = reinterpret_cast<int *>(static_cast<char *>(cand[0]) + kCalibOut);
+  a.candidates = kFrameCandidates;
+  void *args[] = {&a};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(attnres_frame_calibration_kernel),
+                                 dim3(kCalibWgs), dim3(kWave), args, 0, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  int out[kCalibWgs * (1 + kFrameCandidates)];
+  if (e == hipSuccess) e = hipMemcpy(out, a.out, sizeof out, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  for (auto &row : ticks)
+    for (int &v : row) v = INT_MAX;
+  for (int b = 0; b < kCalibWgs; ++b) {
+    const int *o = out + b * (1 + kFrameCandidates);
+    const int x = o[0] & 7;
+    for (int c = 0; c < kFrameCandidates; ++c) ticks[x][c] = std::min(ticks[x][c], o[1 + c]);
+  }
+  for (auto &row : ticks)
+    if (row[0] == INT_MAX)
+      for (int &v : row) v = 0;
+  return hipSuccess;
+}
+
 int init_device_locked(int device) {
   if (g_ws[device].base) return ATTNRES_OK;
   int prev = 0;
   hipError_t e = hipGetDevice(&prev);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e);
-  void *base = nullptr;
+  // Candidate frames, each its own 2 MB allocation; consecutive ones have
+  // alternated between the two halves of the chip.
+  void *cand[kFrameCandidates] = {};
   hipEvent_t ev = nullptr;
-  e = hipMalloc(&base, kWorkspaceBytes);
-  if (e == hipSuccess) e = hipMemset(base, 0, kWorkspaceBytes);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+  for (int c = 0; c < kFrameCandidates && e == hipSuccess; ++c) {
+    e = hipMalloc(&cand[c], kFrameBytes);
+    if (e == hipSuccess) e = hipMemset(cand[c], 0, kFrameBytes);
+  }
+  int ticks[8][kFrameCandidates];
+  if (e == hipSuccess) e = calibrate_frames(cand, ticks);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
   if (e != hipSuccess) {
-    if (base) (void)hipFree(base);
+    for (void *c : cand)
+      if (c) (void)hipFree(c);
     (void)hipSetDevice(prev);
     return hip_fail(e);
   }
+  // The pair of frames whose nearer member serves every XCD fastest.
+  int fa = 0, fb = 1;
+  long best = -1;
+  for (int i = 0; i < kFrameCandidates; ++i)
+    for (int j = i + 1; j < kFrameCandidates; ++j) {
+      long cost = 0;
+      for (int x = 0; x < 8; ++x) cost += std::min(ticks[x][i], ticks[x][j]);
+      if (best < 0 || cost < best) {
+        best = cost;
+        fa = i;
+        fb = j;
+      }
+    }
+  unsigned near = 0;
+  for (int x = 0; x < 8; ++x)
+    if (ticks[x][fb] < ticks[x][fa]) near |= 1u << x;
+  for (int c = 0; c < kFrameCandidates; ++c)
+    if (c != fa && c != fb) (void)hipFree(cand[c]);
   DeviceWorkspace &w = g_ws[device];
-  w.base = base;
+  w.base = cand[fa];
+  w.base_b = cand[fb];
+  w.near = near;
   w.handoff = ev;
-  w.part = static_cast<uint64_t *>(base);
-  w.flag = reinterpret_cast<unsigned *>(static_cast<char *>(base) + kPartBytes);
+  w.part = static_cast<uint64_t *>(w.base);
+  w.part_b = static_cast<uint64_t *>(w.base_b);
+  w.flag = reinterpret_cast<unsigned *>(static_cast<char *>(w.base) + kPartBytes);
   (void)hipSetDevice(prev);
   return ATTNRES_OK;
 }
@@ -2129,8 +2277,10 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
         rc = static_scratch_locked(dev);
         if (rc != ATTNRES_OK) return rc;
       }
-      kp.ws_part = static_cast<uint64_t *>(g_scratch[dev]);
+      // One frame: both copies are the static array.
+      kp.ws_part = kp.ws_part_b = static_cast<uint64_t *>(g_scratch[dev]);
       kp.ws_flag = reinterpret_cast<unsigned *>(static_cast<char *>(g_scratch[dev]) + kPartBytes);
+      kp.ws_by_part = g_frames_mode.load() >= 256;
     }
     DeviceWorkspace &w = g_ws[dev];
     if (noalloc) {
@@ -2151,7 +2301,11 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
     }
     if (!noalloc) {
       kp.ws_part = w.part;
+      kp.ws_part_b = w.part_b;
       kp.ws_flag = w.flag;
+      const int fm = g_frames_mode.load();
+      kp.ws_near = fm < 0 ? w.near : fm >= 256 ? 0xAAAAu : unsigned(fm);
+      kp.ws_by_part = fm >= 256;
     }
   }
 
@@ -2396,6 +2550,7 @@ extern "C" void attnres_shutdown(void) {
       (void)hipSetDevice(d);
       (void)hipDeviceSynchronize();
       (void)hipFree(g_ws[d].base);
+      if (g_ws[d].base_b) (void)hipFree(g_ws[d].base_b);
       if (g_ws[d].handoff) (void)hipEventDestroy(g_ws[d].handoff);
       (void)hipSetDevice(prev);
       g_ws[d] = DeviceWorkspace{};
@@ -2406,25 +2561,28 @@ extern "C" void attnres_shutdown(void) {
 extern "C" int attnres_device_status(int device) {
   if (device < 0 || device >= kMaxDevices) return ATTNRES_E_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  // The allocated workspace and, once attnres_fwd_noalloc has used it on this
-  // device, the static scratch.
-  void *bases[2] = {g_ws[device].base, g_scratch[device]};
-  if (!bases[0] && !bases[1]) return ATTNRES_OK;
+  // The allocated workspace (frames A and B) and, once attnres_fwd_noalloc
+  // has used it on this device, the static scratch; the flag is in the first.
+  void *const bases[2][2] = {{g_ws[device].base, g_ws[device].base_b},
+                             {g_scratch[device], nullptr}};
+  if (!bases[0][0] && !bases[1][0]) return ATTNRES_OK;
   int prev = 0;
   hipError_t e = hipGetDevice(&prev);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e);
   e = hipDeviceSynchronize();
   int rc = ATTNRES_OK;
-  for (void *base : bases) {
+  for (const auto &frames : bases) {
+    void *const base = frames[0];
     if (!base || e != hipSuccess) continue;
     unsigned flag = 0;
     e = hipMemcpy(&flag, static_cast<char *>(base) + kPartBytes, sizeof flag,
                   hipMemcpyDeviceToHost);
     if (e == hipSuccess && flag != 0) {
       // A wait gave up: parts of a token may disagree on the generation, so
-      // restart every word at generation zero.
+      // restart every word, in both frames, at generation zero.
       e = hipMemset(base, 0, kWorkspaceBytes);
+      if (e == hipSuccess && frames[1]) e = hipMemset(frames[1], 0, kPartBytes);
       if (e == hipSuccess) e = hipDeviceSynchronize();
       rc = ATTNRES_E_DEVICE_WAIT;
     }
@@ -2438,6 +2596,12 @@ extern "C" int attnres_last_hip_error(void) { return g_last_hip.load(); }
 
 extern "C" int attnres_debug_force_wait_failure(int enable) {
   g_force_wait_failure.store(enable != 0);
+  return ATTNRES_OK;
+}
+
+extern "C" int attnres_debug_workspace_frames(int mode) {
+  if (mode < -1 || mode > 256) return ATTNRES_E_SHAPE;
+  g_frames_mode.store(mode);
   return ATTNRES_OK;
 }
 
