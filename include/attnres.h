@@ -71,7 +71,7 @@ extern "C" {
 
 /* ---- path selectors for attnres_fwd_path -------------------------------- */
 #define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: at H = 7168 split for T up to
-                                -/56/48/64/64/72/72/72/72 with 0..8 blocks (never with
+                                -/40/48/64/64/72/64/64/60 with 0..8 blocks (never with
                                 0 blocks), else row; above 7168 split with 1..8 blocks
                                 for T <= 48 up to H = 8192 and for T <= 72 beyond,
                                 else any-H; below 7168 split above H = 4096 for

@@ -1910,7 +1910,7 @@ bool cache_rewritten(const FwdArgs &a) {
 // 14 CUs (split) beats one CU per token (row) up to this many tokens, by
 // block count.  A single source (nb = 0) needs no exchange on the row path,
 // which is then faster at every T.
-constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 56, 48, 64, 64, 72, 72, 72, 72};
+constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 48, 64, 64, 72, 64, 64, 60};
 static_assert(72 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
 Kind auto_kind(int64_t T, int nb) {
   return nb > 0 && T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow;

@@ -44,16 +44,17 @@ def test_library_exports_every_declared_symbol(A):
 
 def test_automatic_kernel_choice(A):
     """attnres_auto_path, the choice attnres_fwd makes, against the
-    documented rule.  At 7168: split up to 56/48/64/64/72/72/72/72 tokens
+    documented rule.  At 7168: split up to 40/48/64/64/72/64/64/60 tokens
     for 1..8 block rows, else the tuned row kernel, and row at every T with
     no block rows.  Above 7168: split up to 48 tokens with block rows while
     H <= 8192 and up to 72 beyond, else the any-H kernel.  Below: split up to
     48 tokens with block rows above H = 4096; at 4096 up to 32 with 7-8
     block rows and up to 16 with 5-6; from 2560 to below 4096, except at
     multiples of 1024, up to 16 with block rows; else the any-H kernel.  Host only."""
-    split_max = [None, 56, 48, 64, 64, 72, 72, 72, 72]
+    split_max = [None, 40, 48, 64, 64, 72, 64, 64, 60]
     for nb in range(9):
-        for T in (0, 1, 2, 39, 40, 41, 48, 49, 56, 57, 64, 65, 80, 81, 256, 1024, 8192):
+        for T in (0, 1, 2, 39, 40, 41, 48, 49, 56, 57, 60, 61, 64, 65, 72, 73, 80, 81, 256,
+                  1024, 8192):
             want = (A.ATTNRES_PATH_SPLIT if nb > 0 and T <= split_max[nb]
                     else A.ATTNRES_PATH_ROW)
             assert A.attnres_auto_path(T, 7168, nb) == want, (T, nb)
