@@ -76,7 +76,7 @@
 #define ATTNRES_SPLIT_DPP_WORDS 8       // split path: words summed by DPP instead of via LDS
 #endif
 #ifndef ATTNRES_SPLIT_MFMA_WORDS
-#define ATTNRES_SPLIT_MFMA_WORDS 40     // split path: from this many words, one matrix-core product
+#define ATTNRES_SPLIT_MFMA_WORDS 35     // split path: from this many words, one matrix-core product
 #endif
 #ifndef ATTNRES_ANYH_STAGED
 #define ATTNRES_ANYH_STAGED 1           // any-H: three bank rows staged in LDS where it pays
@@ -1493,9 +1493,10 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
   // tagged words (lane v holds word v).  A few words are summed with DPP
   // wave reductions (independent chains); more are transposed through LDS so
   // that lane v sums value v over the wave; the most (an output norm's Gram
-  // matrix at nb >= 7) come from one matrix-core product.  Measured at T = 1
-  // with an output norm, transposition / product: nb = 5 4.47 / 4.54 us,
-  // nb = 6 4.71 / 4.72, nb = 7 4.84 / 4.79, nb = 8 5.07 / 4.89.
+  // matrix at nb >= 6) come from one matrix-core product.  Measured at T = 1
+  // with an output norm, transposition / product: nb = 4 3.78 / 3.91 us,
+  // nb = 5 3.97 / 4.03, nb = 6 4.12 / 4.09; earlier, nb = 7 4.84 / 4.79 and
+  // nb = 8 5.07 / 4.89.
   if constexpr (NV <= ATTNRES_SPLIT_DPP_WORDS) {
     float ss[NS], dq[NS], val[NV];
     tk.partials(qh, ql, ss, dq);
