@@ -51,4 +51,15 @@ int validate_partial(const FwdArgs &a, const void *partial, int64_t bytes);
 inline int64_t row_stride(int64_t given, int64_t T, int64_t H) { return T <= 1 ? H : given; }
 const char *strerror_text(int status);
 
+// The split path's workspace frames.  ticks[x][c]: the set-up timing of
+// candidate frame c from XCD x (smaller is nearer; INT_MAX where XCD x ran no
+// timing workgroup).  Picks the pair {fa, fb} (fa < fb) whose nearer member
+// gives the least total over the XCDs that were timed, the lowest indices on
+// a tie, and sets bit x of *near when frame fb is strictly nearer XCD x than
+// fa.  Host only.
+constexpr int kFrameXcds = 8;
+constexpr int kFrameCandidates = 4;
+void choose_frames(const int (&ticks)[kFrameXcds][kFrameCandidates], int *fa, int *fb,
+                   unsigned *near);
+
 }  // namespace attnres

@@ -1658,8 +1658,7 @@ __global__ void __launch_bounds__(kPartThreads) attnres_split_kernel(KParams p) 
 // workspace frames: which one is nearer each XCD
 // ---------------------------------------------------------------------------
 
-constexpr int kFrameCandidates = 4;  // 2 MB allocations timed at set-up
-constexpr int kCalibWgs = 64;        // eight per XCD
+constexpr int kCalibWgs = 64;        // eight per XCD (kFrameCandidates 2 MB frames timed)
 constexpr int kCalibRounds = 8;
 
 struct CalibArgs {
@@ -2039,9 +2038,9 @@ int hip_fail(hipError_t e) {
 
 // Times a device-scope store and load from every XCD to each candidate frame
 // (the calibration kernel); ticks[x][c] is the fastest workgroup on XCD x,
-// and an XCD that ran none (a partition with fewer) counts the same for all.
+// INT_MAX for an XCD that ran none (a partition with fewer).
 hipError_t calibrate_frames(void *const (&cand)[kFrameCandidates],
-                            int (&ticks)[8][kFrameCandidates]) {
+                            int (&ticks)[kFrameXcds][kFrameCandidates]) {
   CalibArgs a{};
   for (int c = 0; c < kFrameCandidates; ++c)
     a.lines[c] = reinterpret_cast<uint64_t *>(static_cast<char *>(cand[c]) + kCalibLines);
@@ -2058,12 +2057,9 @@ hipError_t calibrate_frames(void *const (&cand)[kFrameCandidates],
     for (int &v : row) v = INT_MAX;
   for (int b = 0; b < kCalibWgs; ++b) {
     const int *o = out + b * (1 + kFrameCandidates);
-    const int x = o[0] & 7;
+    const int x = o[0] & (kFrameXcds - 1);
     for (int c = 0; c < kFrameCandidates; ++c) ticks[x][c] = std::min(ticks[x][c], o[1 + c]);
   }
-  for (auto &row : ticks)
-    if (row[0] == INT_MAX)
-      for (int &v : row) v = 0;
   return hipSuccess;
 }
 
@@ -2081,7 +2077,7 @@ int init_device_locked(int device) {
     e = hipMalloc(&cand[c], kFrameBytes);
     if (e == hipSuccess) e = hipMemset(cand[c], 0, kFrameBytes);
   }
-  int ticks[8][kFrameCandidates];
+  int ticks[kFrameXcds][kFrameCandidates];
   if (e == hipSuccess) e = calibrate_frames(cand, ticks);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -2092,20 +2088,8 @@ int init_device_locked(int device) {
   }
   // The pair of frames whose nearer member serves every XCD fastest.
   int fa = 0, fb = 1;
-  long best = -1;
-  for (int i = 0; i < kFrameCandidates; ++i)
-    for (int j = i + 1; j < kFrameCandidates; ++j) {
-      long cost = 0;
-      for (int x = 0; x < 8; ++x) cost += std::min(ticks[x][i], ticks[x][j]);
-      if (best < 0 || cost < best) {
-        best = cost;
-        fa = i;
-        fb = j;
-      }
-    }
   unsigned near = 0;
-  for (int x = 0; x < 8; ++x)
-    if (ticks[x][fb] < ticks[x][fa]) near |= 1u << x;
+  choose_frames(ticks, &fa, &fb, &near);
   for (int c = 0; c < kFrameCandidates; ++c)
     if (c != fa && c != fb) (void)hipFree(cand[c]);
   DeviceWorkspace &w = g_ws[device];

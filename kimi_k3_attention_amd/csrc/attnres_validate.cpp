@@ -12,6 +12,7 @@
 // 16-byte vector accesses and the in-place writes.
 #include "attnres_internal.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -259,3 +260,30 @@ extern "C" int attnres_validate(const void *prefix, const void *delta, const voi
 }
 
 extern "C" const char *attnres_strerror(int status) { return attnres::strerror_text(status); }
+
+namespace attnres {
+
+void choose_frames(const int (&ticks)[kFrameXcds][kFrameCandidates], int *fa, int *fb,
+                   unsigned *near) {
+  *fa = 0;
+  *fb = 1;
+  int64_t best = -1;
+  for (int i = 0; i < kFrameCandidates; ++i)
+    for (int j = i + 1; j < kFrameCandidates; ++j) {
+      int64_t cost = 0;
+      for (int x = 0; x < kFrameXcds; ++x) {
+        if (ticks[x][i] == INT_MAX && ticks[x][j] == INT_MAX) continue;  // not timed
+        cost += ticks[x][i] < ticks[x][j] ? ticks[x][i] : ticks[x][j];
+      }
+      if (best < 0 || cost < best) {
+        best = cost;
+        *fa = i;
+        *fb = j;
+      }
+    }
+  *near = 0;
+  for (int x = 0; x < kFrameXcds; ++x)
+    if (ticks[x][*fb] < ticks[x][*fa]) *near |= 1u << x;
+}
+
+}  // namespace attnres

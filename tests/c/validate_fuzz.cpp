@@ -4,7 +4,9 @@
 // through validate, validate_partial and partial_bytes.  Every call must
 // return a documented status (no crash, no overflow, no out-of-range shift);
 // a few fixed cases pin the answer.  Built and run by tests/test_boundary.py
-// with g++ (host code only); prints "ok <calls>" on success.
+// with g++ (host code only); prints "ok <calls>" on success.  Also pins the
+// choice of the split path's two workspace frames from set-up timings.
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -119,6 +121,38 @@ int main() {
     std::printf("fixed cases: %d %d %d %d %lld\n", validate(v), validate(big_t), validate(big_h),
                 validate(big_stride), static_cast<long long>(partial_bytes(4, 7168)));
     return 1;
+  }
+  // The workspace frames' choice: two XCD halves that each find a different
+  // pair member near, ties, and XCDs that ran no timing workgroup.
+  {
+    int ticks[kFrameXcds][kFrameCandidates];
+    for (int x = 0; x < kFrameXcds; ++x)
+      for (int c = 0; c < kFrameCandidates; ++c)
+        ticks[x][c] = ((x < 4) == (c % 2 == 0)) ? 30 : 55;  // even frames near XCDs 0-3
+    int fa = -1, fb = -1;
+    unsigned near = 0;
+    choose_frames(ticks, &fa, &fb, &near);
+    if (fa != 0 || fb != 1 || near != 0xF0u) {
+      std::printf("frames: alternating halves gave %d %d %x\n", fa, fb, near);
+      return 1;
+    }
+    for (auto &row : ticks)
+      for (int &v : row) v = 40;
+    choose_frames(ticks, &fa, &fb, &near);
+    if (fa != 0 || fb != 1 || near != 0u) {
+      std::printf("frames: equal timings gave %d %d %x\n", fa, fb, near);
+      return 1;
+    }
+    // frames 2 and 3 are the good pair; XCDs 5-7 were not timed
+    for (int x = 0; x < kFrameXcds; ++x)
+      for (int c = 0; c < kFrameCandidates; ++c)
+        ticks[x][c] = x >= 5 ? INT_MAX : c == 3 ? (x < 2 ? 20 : 60) : c == 2 ? (x < 2 ? 60 : 20) : 70;
+    choose_frames(ticks, &fa, &fb, &near);
+    if (fa != 2 || fb != 3 || near != 0x3u) {
+      std::printf("frames: partial timing gave %d %d %x\n", fa, fb, near);
+      return 1;
+    }
+    calls += 3;
   }
   std::printf("ok %ld\n", calls);
   return 0;
