@@ -379,7 +379,8 @@ def test_validation_under_sanitizers(tmp_path):
     plain C++), built with g++ under the address and undefined-behaviour
     sanitizers, through tests/c/validate_fuzz.cpp: 600,000 calls with
     plausible and extreme sizes, strides, indices, epsilons and pointers
-    return only documented statuses, with no overflow or bad access."""
+    return only documented statuses, with no overflow or bad access; and the
+    choice of the split path's two workspace frames from set-up timings."""
     import shutil
     import subprocess
     if shutil.which("g++") is None:
