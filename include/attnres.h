@@ -72,13 +72,12 @@ extern "C" {
 /* ---- path selectors for attnres_fwd_path -------------------------------- */
 #define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: at H = 7168 split for T up to
                                 -/40/48/64/64/72/64/64/60 with 0..8 blocks (never with
-                                0 blocks), else row; above 7168 split with 1..8 blocks
-                                for T <= 48 up to H = 8192 and for T <= 72 beyond,
-                                else any-H; below 7168 split above H = 4096 for
-                                T <= 48 with 1..8 blocks, at H = 4096 for T <= 32
-                                with 7..8 blocks and T <= 16 with 5..6, from 2560 to
-                                below 4096 (not multiples of 1024) for T <= 16 with
-                                1..8 blocks, else any-H */
+                                0 blocks), else row; elsewhere the any-H kernel,
+                                except split with 1..8 blocks for T up to 72 above
+                                H = 8192, 16/24/32/40/32/32/32/40 from 7176 to 8192,
+                                8/16/24/40/40/48/48/48 from 4104 to 7160, 8 with 7
+                                blocks and 16 with 8 at 4096, and 8 with 8 blocks
+                                from 3080 to 4088 */
 #define ATTNRES_PATH_ROW 1   /* one workgroup per token (the any-H kernel when H != 7168) */
 #define ATTNRES_PATH_SPLIT 2 /* hidden dim split over 14 workgroups per token (any H,
                                 T <= 256) */

@@ -1915,46 +1915,46 @@ static_assert(72 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the worksp
 Kind auto_kind(int64_t T, int nb) {
   return nb > 0 && T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow;
 }
-// Above H = 7168 (2-3 segments per lane and part) the split path wins up to
-// about 48 tokens with 1-8 blocks while H <= 8192, where the any-H row kernel
-// is relatively fast (H = 8192, nb = 8: T = 48 split 7.6 against 8.2 us,
-// T = 64 8.5 against 8.4), and up to 72 tokens beyond (H = 9216-16384, every
-// nb and T up to 72; H = 16384, nb = 8: T = 72 12.0 against 13.7 us, T = 80
-// 17.6 against 13.9).
-constexpr int kSplitMaxTWide = 48;
-constexpr int kSplitMaxTWider = 72;
+// Away from H = 7168, from latency grids against the any-H row kernel (graph
+// replay, cold inputs, delta and output norm; us per call, any-H / split).
+// Above 8192 (2-3 segments per lane and part) the split path leads at every
+// block count up to 72 tokens (H = 10240, nb = 8, T = 72: 10.64 / 8.93;
+// H = 16384, nb = 8, T = 80: 13.04 / 16.06).  From 7176 to 8192 the any-H
+// kernel is relatively fast and the split path's reach depends on the block
+// count (H = 8192: nb = 1 leads to T = 16, T = 24 4.32 / 4.35; nb = 8 to
+// T = 40, T = 48 7.47 / 7.60; H = 7680 alike).  Between 4096 and 7168 (one
+// masked segment per lane and part) likewise, measured at 4608, 5120 and
+// 6144 (H = 5120: nb = 1 ties at T = 8, 3.75 / 3.74; nb = 4 leads to T = 40,
+// T = 48 4.92 / 5.00; nb = 8 still leads at T = 48, 6.40 / 6.12).  At 4096
+// and below the any-H kernel leads almost everywhere: only nb = 8 (at 4096
+// also nb = 7) gains, by at most 3 %, at a few tokens (H = 4096, nb = 8,
+// T = 16: 4.81 / 4.79; T = 24: 4.84 / 5.02; H = 3584, nb = 8, T = 1: 4.34 /
+// 4.20; H = 2880 and 3072: never).
 constexpr int64_t kWiderHidden = 8192;
-// Below H = 7168 (one masked segment per lane and part) the any-H row kernel
-// is faster at H <= 3072.  Above 4096 the split path leads with 1-8 blocks up
-// to 48 tokens (H = 4608, nb = 4, T = 48: 5.0 against 6.0 us; H = 6144,
-// nb = 8: 6.5 against 7.5).  At 4096, which suits the any-H kernel, it leads
-// with 7-8 blocks up to 32 tokens and with 5-6 up to 16 (nb = 8, T = 32: 5.4
-// against 5.6 us; nb = 6, T = 32: a tie; nb = 4: a tie up to T = 16).
+constexpr int kSplitMaxTWider = 72;
+constexpr int kSplitMaxTWide[kMaxBlocks + 1] = {0, 16, 24, 32, 40, 32, 32, 32, 40};
 constexpr int64_t kNarrowSplitHidden = 4096;
-constexpr int kSplitMaxTNarrow = 48;
-constexpr int kSplitMaxTNarrow7 = 32;   // at 4096 with 7 or 8 blocks
-constexpr int kSplitMaxTNarrow5 = 16;   // at 4096 with 5 or 6 blocks
-// From 2560 up to 4096 the any-H kernel is strong at the multiples of 1024
-// (3072: ahead at nb = 1 and 4) and weaker between them, where the split path
-// leads or ties up to 16 tokens at every block count (H = 3584, nb = 8,
-// T = 1: 4.5 against 5.6 us; H = 2560, nb = 1, T = 16: a tie).
-constexpr int64_t kOddSplitHidden = 2560;
-constexpr int kSplitMaxTOdd = 16;
+constexpr int kSplitMaxTNarrow[kMaxBlocks + 1] = {0, 8, 16, 24, 40, 40, 48, 48, 48};
+constexpr int kSplitMaxT4096[kMaxBlocks + 1] = {0, 0, 0, 0, 0, 0, 0, 8, 16};
+constexpr int64_t kSmallSplitHidden = 3072;  // above it (below 4096): nb = 8 only
+constexpr int kSplitMaxTSmall8 = 8;
 
 // The kernel attnres_fwd runs for T tokens, hidden size H and nb block rows.
 Kind auto_choice(int64_t T, int64_t H, int nb) {
   if (H == kHidden) return auto_kind(T, nb);
-  if (H > kHidden && nb > 0 && T <= (H > kWiderHidden ? kSplitMaxTWider : kSplitMaxTWide))
-    return Kind::kSplit;
-  if (H < kHidden && H > kNarrowSplitHidden && nb > 0 && T <= kSplitMaxTNarrow)
-    return Kind::kSplit;
-  if (H == kNarrowSplitHidden &&
-      ((nb >= 7 && T <= kSplitMaxTNarrow7) || (nb >= 5 && T <= kSplitMaxTNarrow5)))
-    return Kind::kSplit;
-  if (H >= kOddSplitHidden && H < kNarrowSplitHidden && H % 1024 != 0 && nb > 0 &&
-      T <= kSplitMaxTOdd)
-    return Kind::kSplit;
-  return Kind::kAnyH;
+  if (nb <= 0) return Kind::kAnyH;
+  int64_t limit = 0;
+  if (H > kWiderHidden)
+    limit = kSplitMaxTWider;
+  else if (H > kHidden)
+    limit = kSplitMaxTWide[nb];
+  else if (H > kNarrowSplitHidden)
+    limit = kSplitMaxTNarrow[nb];
+  else if (H == kNarrowSplitHidden)
+    limit = kSplitMaxT4096[nb];
+  else if (H > kSmallSplitHidden && nb == kMaxBlocks)
+    limit = kSplitMaxTSmall8;
+  return T <= limit ? Kind::kSplit : Kind::kAnyH;
 }
 
 KernelFn pick(Kind kind, int nb, bool d, bool o, bool cache_rw) {

@@ -46,11 +46,11 @@ def test_automatic_kernel_choice(A):
     """attnres_auto_path, the choice attnres_fwd makes, against the
     documented rule.  At 7168: split up to 40/48/64/64/72/64/64/60 tokens
     for 1..8 block rows, else the tuned row kernel, and row at every T with
-    no block rows.  Above 7168: split up to 48 tokens with block rows while
-    H <= 8192 and up to 72 beyond, else the any-H kernel.  Below: split up to
-    48 tokens with block rows above H = 4096; at 4096 up to 32 with 7-8
-    block rows and up to 16 with 5-6; from 2560 to below 4096, except at
-    multiples of 1024, up to 16 with block rows; else the any-H kernel.  Host only."""
+    no block rows.  Elsewhere the any-H kernel except: above 8192, split up
+    to 72 tokens with block rows; from 7176 to 8192 up to
+    16/24/32/40/32/32/32/40 tokens; from 4104 to 7160 up to
+    8/16/24/40/40/48/48/48; at 4096 up to 8 with 7 block rows and 16 with
+    8; from 3080 to 4088 up to 8 with 8 block rows.  Host only."""
     split_max = [None, 40, 48, 64, 64, 72, 64, 64, 60]
     for nb in range(9):
         for T in (0, 1, 2, 39, 40, 41, 48, 49, 56, 57, 60, 61, 64, 65, 72, 73, 80, 81, 256,
@@ -58,19 +58,28 @@ def test_automatic_kernel_choice(A):
             want = (A.ATTNRES_PATH_SPLIT if nb > 0 and T <= split_max[nb]
                     else A.ATTNRES_PATH_ROW)
             assert A.attnres_auto_path(T, 7168, nb) == want, (T, nb)
-    for H in (7176, 8192, 8200, 14344, 16384):
+    wide = [0, 16, 24, 32, 40, 32, 32, 32, 40]
+    narrow = [0, 8, 16, 24, 40, 40, 48, 48, 48]
+    at4096 = [0, 0, 0, 0, 0, 0, 0, 8, 16]
+
+    def limit(H, nb):
+        if nb == 0:
+            return -1
+        if H > 8192:
+            return 72
+        if H > 7168:
+            return wide[nb]
+        if H > 4096:
+            return narrow[nb]
+        if H == 4096:
+            return at4096[nb]
+        return 8 if (H > 3072 and nb == 8) else -1
+
+    for H in (8, 2048, 2552, 2560, 2880, 3072, 3080, 3584, 4088, 4096, 4104, 5120, 7160,
+              7176, 7680, 8192, 8200, 14344, 16384):
         for nb in range(9):
-            for T in (1, 48, 49, 72, 73, 1024):
-                limit = 48 if H <= 8192 else 72
-                want = A.ATTNRES_PATH_SPLIT if nb > 0 and T <= limit else A.ATTNRES_PATH_ANY_H
-                assert A.attnres_auto_path(T, H, nb) == want, (T, H, nb)
-    for H in (8, 2048, 2552, 2560, 3072, 3584, 4088, 4096, 4104, 5120, 7160):
-        for nb in range(9):
-            for T in (1, 16, 17, 32, 33, 48, 49, 1024):
-                split = nb > 0 and ((H > 4096 and T <= 48) or
-                                    (H == 4096 and ((nb >= 7 and T <= 32) or (nb >= 5 and T <= 16))) or
-                                    (2560 <= H < 4096 and H % 1024 != 0 and T <= 16))
-                want = A.ATTNRES_PATH_SPLIT if split else A.ATTNRES_PATH_ANY_H
+            for T in (1, 8, 9, 16, 17, 24, 25, 32, 33, 40, 41, 48, 49, 72, 73, 1024):
+                want = A.ATTNRES_PATH_SPLIT if T <= limit(H, nb) else A.ATTNRES_PATH_ANY_H
                 assert A.attnres_auto_path(T, H, nb) == want, (T, H, nb)
     for (T, H, nb), err in (((1, 7170, 8), "ATTNRES_E_UNSUPPORTED"),
                             ((1, 16392, 8), "ATTNRES_E_UNSUPPORTED"),
