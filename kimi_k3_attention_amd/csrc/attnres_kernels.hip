@@ -1284,8 +1284,9 @@ static_assert(3 * kParts * kPartThreads * kSeg >= kMaxHidden,
 // a reader needs one round trip once the words are there.  (A load with only
 // the workgroup-scope bit would be served from the reading CU's own L1 and
 // never see a partner's store.)  A part's generation for this
-// call is its own word 0's generation plus one: every call rewrites word 0 of
-// all kParts parts of a token with the same generation, so the parts agree
+// call is one past the later of its own word 0's generations in the two
+// frames below: every call rewrites word 0 of all kParts parts of a token
+// with the same generation, in one frame or the other, so the parts agree
 // without communicating (the workspace starts at zero).  Waits are bounded; a
 // wait that gives up raises the device flag.
 __device__ __forceinline__ uint64_t tagged_load(const uint64_t *w) {
