@@ -40,7 +40,7 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 # The mid-prefill call's kernel: 8 block rows, delta, output norm, and the
 # two rewritten rows read through the cache (T >= 1024, written slot 3 < 8).
-DOMINANT_KERNEL = "attnres_row_kernel<8, true, true, true>"
+DOMINANT_KERNEL = "attnres_row_kernel<8, true, true, true, false>"
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "attnres_row_kernel_mid_prefill_T1024_traffic.json")
 CALIBRATION_BYTES = 512 << 20

@@ -71,7 +71,7 @@ extern "C" {
 
 /* ---- path selectors for attnres_fwd_path -------------------------------- */
 #define ATTNRES_PATH_AUTO 0  /* what attnres_fwd does: at H = 7168 split for T up to
-                                -/40/48/64/64/72/64/64/60 with 0..8 blocks (never with
+                                -/40/40/48/56/56/52/60/56 with 0..8 blocks (never with
                                 0 blocks), else row; elsewhere the any-H kernel,
                                 except split with 1..8 blocks for T up to 72 above
                                 H = 8192, 16/24/32/40/32/32/32/40 from 7176 to 8192,

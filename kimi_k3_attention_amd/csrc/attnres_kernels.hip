@@ -113,6 +113,14 @@ constexpr int kBufferFormat = 0x00020000;
 constexpr int kAuxNt = 2;  // cache-policy operand of a load: non-temporal
 constexpr float kInvHidden = 1.0f / kHidden;
 
+// Row path: calls of at most kRowRangedMaxT tokens with two or more bank
+// rows read them with range-checked loads (the row kernel's RANGED form).
+// Measured against plain loads, bit-identical, T = 32-128 at nb = 2-8:
+// 1.3-3.7 % faster; T = 192 within 0.7 %; T = 256-768 up to 3.8 % slower;
+// nb = 1 no faster at any T.
+constexpr int kRowRangedMinBlocks = 2;
+constexpr int kRowRangedMaxT = 128;
+
 // Row path grid.  With few source rows a token moves little data, and with
 // one workgroup per token the whole grid is resident at once, so every token
 // loads, computes and stores in lockstep; a persistent grid of three
@@ -838,13 +846,18 @@ __device__ __forceinline__ float wave_sum_of_partials(const float *v, int n) {
 // The grid either has one workgroup per token or is persistent (a few
 // workgroups per CU looping over tokens); LDS partials are double-buffered by
 // iteration parity so one barrier per phase suffices.
-template <int NB, bool DELTA, bool ONORM, bool CACHE_RW = false>
+// RANGED: rows and weights are read with range-checked (buffer) loads, the
+// form the masked kernels use, here over whole rows (nothing is cut off).
+// Small calls take it (kRowRangedMaxT): with one token per workgroup they
+// wait on each load's latency, and this form issues them sooner.
+template <int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, bool RANGED = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kRowThreads, kRowThreads),
                                // the unified arch+acc register file counts double
                                amdgpu_num_vgpr(ATTNRES_ROW_MAX_VGPRS / 2)))
 attnres_row_kernel(KParams p) {
   constexpr int NS = NB + 1;
   constexpr int SPL = kRowSegsPerLane;
+  static_assert(!(RANGED && CACHE_RW), "the ranged form reads every row streaming");
   // cur's in-place writes as soon as every load has landed, in the variant
   // that read those rows through the cache (calls of T * H >= 1024 * 7168):
   // there T = 1024 with 4 or 8 bank rows measured 1.2-1.8 % faster, T =
@@ -911,7 +924,7 @@ attnres_row_kernel(KParams p) {
     return;
   }
   for (int64_t t = blockIdx.x; t < p.T; t += t_step, par ^= 1) {
-    Token<NB, DELTA, ONORM, SPL, false, CACHE_RW> tk;
+    Token<NB, DELTA, ONORM, SPL, RANGED, CACHE_RW> tk;
     tk.issue(p, t, seg0, seg_step);
     if constexpr (NB == 0) {
       // One source, weight exactly 1: y = cur, no logit, and the output
@@ -1734,11 +1747,19 @@ __global__ void __launch_bounds__(kWave) attnres_frame_calibration_kernel(CalibA
 using KernelFn = void (*)(KParams);
 
 template <int NB>
-KernelFn row_fn(bool d, bool o, bool cache_rw) {
+KernelFn row_fn(bool d, bool o, bool cache_rw, bool ranged) {
   if constexpr (NB > 0)
     if (cache_rw) {
       if (d) return o ? attnres_row_kernel<NB, true, true, true> : attnres_row_kernel<NB, true, false, true>;
       return o ? attnres_row_kernel<NB, false, true, true> : attnres_row_kernel<NB, false, false, true>;
+    }
+  if constexpr (NB >= kRowRangedMinBlocks)
+    if (ranged) {
+      if (d)
+        return o ? attnres_row_kernel<NB, true, true, false, true>
+                 : attnres_row_kernel<NB, true, false, false, true>;
+      return o ? attnres_row_kernel<NB, false, true, false, true>
+               : attnres_row_kernel<NB, false, false, false, true>;
     }
   if (d) return o ? attnres_row_kernel<NB, true, true> : attnres_row_kernel<NB, true, false>;
   return o ? attnres_row_kernel<NB, false, true> : attnres_row_kernel<NB, false, false>;
@@ -1949,8 +1970,10 @@ bool cache_rewritten(const FwdArgs &a) {
 // (graph replay, cold inputs, delta and output norm): spreading a token over
 // 14 CUs (split) beats one CU per token (row) up to this many tokens, by
 // block count.  A single source (nb = 0) needs no exchange on the row path,
-// which is then faster at every T.
-constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 48, 64, 64, 72, 64, 64, 60};
+// which is then faster at every T.  The row side near these limits is the
+// row kernel's ranged form (kRowRangedMaxT), which moved them down from
+// 48/64/64/72/64/64/60 at nb = 2..8.
+constexpr int kSplitMaxT[kMaxBlocks + 1] = {0, 40, 40, 48, 56, 56, 52, 60, 56};
 static_assert(72 <= ATTNRES_SPLIT_MAX_TOKENS, "split crossover beyond the workspace");
 Kind auto_kind(int64_t T, int nb) {
   return nb > 0 && T <= kSplitMaxT[nb] ? Kind::kSplit : Kind::kRow;
@@ -1997,10 +2020,10 @@ Kind auto_choice(int64_t T, int64_t H, int nb) {
   return T <= limit ? Kind::kSplit : Kind::kAnyH;
 }
 
-KernelFn pick(Kind kind, int nb, bool d, bool o, bool cache_rw) {
+KernelFn pick(Kind kind, int nb, bool d, bool o, bool cache_rw, bool ranged) {
   switch (nb) {
 #define ATTNRES_CASE(N) \
-  case N: return kind == Kind::kSplit ? split_fn<N>(d, o) : row_fn<N>(d, o, cache_rw);
+  case N: return kind == Kind::kSplit ? split_fn<N>(d, o) : row_fn<N>(d, o, cache_rw, ranged);
     ATTNRES_CASE(0) ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4)
     ATTNRES_CASE(5) ATTNRES_CASE(6) ATTNRES_CASE(7) ATTNRES_CASE(8)
 #undef ATTNRES_CASE
@@ -2367,8 +2390,10 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
   // tokens: T = 1024, nb = 8, with a delta: 33.7 -> 32.6 us, T = 4096:
   // 131 -> 117 us.  Smaller calls (latency-bound) read them streaming.
   const bool cache_rw = kind == Kind::kRow && cache_rewritten(a);
+  const bool ranged = kind == Kind::kRow && !cache_rw && a.num_blocks >= kRowRangedMinBlocks &&
+                      a.T <= kRowRangedMaxT;
   KernelFn fn = split && !tuned ? pick_split_masked(a.num_blocks, has_d, has_o, split_spl)
-                              : pick(kind, a.num_blocks, has_d, has_o, cache_rw);
+                              : pick(kind, a.num_blocks, has_d, has_o, cache_rw, ranged);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;
   unsigned row_grid = unsigned(a.T);
   const int wpc = row_wgs_per_cu(a.num_blocks);

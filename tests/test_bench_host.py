@@ -166,7 +166,7 @@ def test_counter_summary_medians_and_ratios(tmp_path, profiles_dir):
     bench.write_counter_summary("c.txt", "t", ["cmd1"], {"k": str(tmp_path / "run")})
     text = (profiles_dir / "c.txt").read_text()
     assert "# command: cmd1" in text
-    kernels = ["attnres_row_kernel<8, true, true, true>", "mid_kernel<true>"]
+    kernels = [bench.DOMINANT_KERNEL, "mid_kernel<true>"]
     assert text.count(" | ".join(["# per-dispatch medians; counter"] + kernels)) == 1
     assert "SQ_WAVE_CYCLES | 6000 | 1000" in text
     assert "wave lifetime, cycles (SQ_WAVE_CYCLES / SQ_WAVES) | 60 | 20" in text

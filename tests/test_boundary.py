@@ -44,16 +44,16 @@ def test_library_exports_every_declared_symbol(A):
 
 def test_automatic_kernel_choice(A):
     """attnres_auto_path, the choice attnres_fwd makes, against the
-    documented rule.  At 7168: split up to 40/48/64/64/72/64/64/60 tokens
+    documented rule.  At 7168: split up to 40/40/48/56/56/52/60/56 tokens
     for 1..8 block rows, else the tuned row kernel, and row at every T with
     no block rows.  Elsewhere the any-H kernel except: above 8192, split up
     to 72 tokens with block rows; from 7176 to 8192 up to
     16/24/32/40/32/32/32/40 tokens; from 4104 to 7160 up to
     8/16/24/40/40/48/48/48; at 4096 up to 8 with 7 block rows and 16 with
     8; from 3080 to 4088 up to 8 with 8 block rows.  Host only."""
-    split_max = [None, 40, 48, 64, 64, 72, 64, 64, 60]
+    split_max = [None, 40, 40, 48, 56, 56, 52, 60, 56]
     for nb in range(9):
-        for T in (0, 1, 2, 39, 40, 41, 48, 49, 56, 57, 60, 61, 64, 65, 72, 73, 80, 81, 256,
+        for T in (0, 1, 2, 39, 40, 41, 48, 49, 52, 53, 56, 57, 60, 61, 64, 65, 72, 73, 80, 81, 256,
                   1024, 8192):
             want = (A.ATTNRES_PATH_SPLIT if nb > 0 and T <= split_max[nb]
                     else A.ATTNRES_PATH_ROW)

@@ -439,6 +439,46 @@ def test_ragged_sizes(G, T, nb, widx):
     _run_and_check_all_paths(G, case)
 
 
+# The row kernel at H = 7168 reads rows with range-checked loads in calls of
+# up to 128 tokens with two or more bank rows, and with plain loads above.
+RANGED_ROW_CASES = [
+    dict(nb=2),
+    dict(nb=3, has_delta=False),
+    dict(nb=4, widx=3),
+    dict(nb=5, has_onorm=False, widx=1),
+    dict(nb=6, widx=0, recipe="student_t"),
+    dict(nb=7, widx=6),
+    dict(nb=8, widx=7, has_delta=False, has_onorm=False),
+]
+
+
+@pytest.mark.parametrize("kw", RANGED_ROW_CASES, ids=lambda kw: f"nb{kw['nb']}")
+def test_row_kernel_small_call_form(G, kw):
+    """The two load forms do the same arithmetic: a 129-token call (plain
+    loads) matches the oracle, and a 128-token call (range-checked loads)
+    on its first 128 tokens gives bit-identical outputs and writes."""
+    from kimi_k3_attention_amd import attnres as A
+    case = W.Case(f"ranged_nb{kw['nb']}", T=129, seed=70 + kw["nb"], **kw)
+    inp = W.make_inputs(case)
+    G.say(case.name, "T=129")
+    d = G.upload(inp)
+    G.run(d, path=A.ATTNRES_PATH_ROW)
+    full = G.download(d)
+    G.check_full(inp, full, G.oracle_full(inp))
+    sub = W.with_(case, T=128)
+    part_in = W.Inputs(case=sub, prefix=inp.prefix[:128].copy(),
+                       delta=None if inp.delta is None else inp.delta[:128].copy(),
+                       bank=inp.bank[:sub.bank_elems].copy(), res_w=inp.res_w, rms_w=inp.rms_w,
+                       onw=inp.onw, out_init=inp.out_init[:128].copy())
+    G.say(case.name, "T=128")
+    d = G.upload(part_in)
+    G.run(d, path=A.ATTNRES_PATH_ROW)
+    part = G.download(d)
+    assert np.array_equal(part.out, full.out[:128]), "out"
+    assert np.array_equal(part.prefix, full.prefix[:128]), "prefix"
+    assert np.array_equal(part.bank, full.bank[:sub.bank_elems]), "bank"
+
+
 @pytest.mark.parametrize("T,nb,widx", [(2500, 1, 0), (1537, 0, -1), (4099, 1, -1)])
 def test_persistent_grid_few_blocks(G, T, nb, widx):
     """Few source rows run a persistent grid (a few workgroups per CU, each
