@@ -618,15 +618,17 @@ def test_cancelling_sources(G):
     assert np.isfinite(y_norm).all()
 
 
-@pytest.mark.parametrize("path_name", ["row", "split", "any_h"])
+@pytest.mark.parametrize("path_name", ["row", "split", "any_h", "row_small"])
 def test_bank_offsets_beyond_32_bits(G, path_name):
     """A bank whose element offsets exceed 2^31 (token stride 2^24 elements,
-    about 4.8 GB): only the used rows are filled; sampled tokens are checked
-    against the oracle and the elements right after each written row keep
-    their sentinel."""
+    about 4.8 GB; for the row kernel's small-call form, 100 tokens 2^25
+    apart, about 6.7 GB): only the used rows are filled; sampled tokens are
+    checked against the oracle and the elements right after each written row
+    keep their sentinel."""
     from kimi_k3_attention_amd import attnres as A
-    path = _path_of(path_name)
-    T, nb, cap, H, ts = 150, 5, 8, 7168, 1 << 24
+    small = path_name == "row_small"
+    path = A.ATTNRES_PATH_ROW if small else _path_of(path_name)
+    T, nb, cap, H, ts = (100, 5, 8, 7168, 1 << 25) if small else (150, 5, 8, 7168, 1 << 24)
     case = W.Case("small_rows", T=T, nb=nb, cap=cap, widx=6, seed=95)
     inp = W.make_inputs(case)                      # dense bank, used for the values
     bank = torch.full((T * ts,), 0x7F81, dtype=torch.int16, device="cuda")
