@@ -2046,6 +2046,8 @@ constexpr size_t kCalibLines = kFrameBytes - 16384;
 constexpr size_t kCalibOut = kFrameBytes - 4096;
 static_assert(kWorkspaceBytes <= kCalibLines, "split workspace overlaps the calibration area");
 static_assert(size_t(kCalibWgs) * 128 <= kCalibOut - kCalibLines, "calibration lines");
+static_assert(sizeof(int) * kCalibWgs * (1 + kFrameCandidates) <= kFrameBytes - kCalibOut,
+              "calibration output");
 static_assert(size_t(kCalibWgs) * (1 + kFrameCandidates) * sizeof(int) <= 4096, "calibration out");
 
 // Split calls on one device must run one after another: they share the
