@@ -88,6 +88,8 @@ def test_noalloc_other_hidden_size_and_row_path(G):
     for k, (kw, path) in enumerate(((dict(T=24, nb=5, H=12288, widx=4), A.ATTNRES_PATH_SPLIT),
                                     (dict(T=9, nb=3, H=2992), A.ATTNRES_PATH_SPLIT),
                                     (dict(T=300, nb=8, widx=3), A.ATTNRES_PATH_ROW),
+                                    # the row kernel's small-call (range-checked) form
+                                    (dict(T=100, nb=4, widx=2), A.ATTNRES_PATH_ROW),
                                     # any-H kernel with three bank rows staged in LDS
                                     (dict(T=300, nb=6, H=12288, widx=5), A.ATTNRES_PATH_ANY_H),
                                     (dict(T=800, nb=8, H=5120, widx=3), A.ATTNRES_PATH_ANY_H))):
