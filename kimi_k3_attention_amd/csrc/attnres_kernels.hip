@@ -113,13 +113,14 @@ constexpr int kBufferFormat = 0x00020000;
 constexpr int kAuxNt = 2;  // cache-policy operand of a load: non-temporal
 constexpr float kInvHidden = 1.0f / kHidden;
 
-// Row path: calls of at most kRowRangedMaxT tokens with two or more bank
-// rows read them with range-checked loads (the row kernel's RANGED form).
-// Measured against plain loads, bit-identical, T = 32-128 at nb = 2-8:
-// 1.3-3.7 % faster; T = 192 within 0.7 %; T = 256-768 up to 3.8 % slower;
-// nb = 1 no faster at any T.
+// Row path: calls of at most kRowRangedMaxT[nb] tokens with two or more
+// bank rows read them with range-checked loads (the row kernel's RANGED
+// form).  Measured against plain loads, bit-identical: T = 32-176 at nb =
+// 2-8 0.3-3.7 % faster, T = 192 0.2-0.8 %; T = 208-256 0.2-1 % slower at
+// nb = 4-8 but 0.8-2.3 % faster at nb = 2; T = 384-768 slower at every nb;
+// nb = 1 no faster at any T.  nb = 3 (not measured) takes 192, as nb = 4-8.
 constexpr int kRowRangedMinBlocks = 2;
-constexpr int kRowRangedMaxT = 128;
+constexpr int kRowRangedMaxT[kMaxBlocks + 1] = {0, 0, 256, 192, 192, 192, 192, 192, 192};
 
 // Row path grid.  With few source rows a token moves little data, and with
 // one workgroup per token the whole grid is resident at once, so every token
@@ -848,8 +849,10 @@ __device__ __forceinline__ float wave_sum_of_partials(const float *v, int n) {
 // iteration parity so one barrier per phase suffices.
 // RANGED: rows and weights are read with range-checked (buffer) loads, the
 // form the masked kernels use, here over whole rows (nothing is cut off).
-// Small calls take it (kRowRangedMaxT): with one token per workgroup they
-// wait on each load's latency, and this form issues them sooner.
+// Small calls take it (kRowRangedMaxT): the compiler then issues the
+// weights' loads (L2 hits) ahead of the rows, where with plain loads it
+// interleaves them with prefix and delta and the fused query waits on an HBM
+// load.  With about one token per CU that wait is not hidden.
 template <int NB, bool DELTA, bool ONORM, bool CACHE_RW = false, bool RANGED = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kRowThreads, kRowThreads),
                                // the unified arch+acc register file counts double
@@ -2393,7 +2396,7 @@ int fwd_impl(const FwdArgs &a, void *stream, int path, bool noalloc = false) {
   // 131 -> 117 us.  Smaller calls (latency-bound) read them streaming.
   const bool cache_rw = kind == Kind::kRow && cache_rewritten(a);
   const bool ranged = kind == Kind::kRow && !cache_rw && a.num_blocks >= kRowRangedMinBlocks &&
-                      a.T <= kRowRangedMaxT;
+                      a.T <= kRowRangedMaxT[a.num_blocks];
   KernelFn fn = split && !tuned ? pick_split_masked(a.num_blocks, has_d, has_o, split_spl)
                               : pick(kind, a.num_blocks, has_d, has_o, cache_rw, ranged);
   if (!fn) return ATTNRES_E_NUM_BLOCKS;

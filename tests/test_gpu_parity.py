@@ -440,7 +440,9 @@ def test_ragged_sizes(G, T, nb, widx):
 
 
 # The row kernel at H = 7168 reads rows with range-checked loads in calls of
-# up to 128 tokens with two or more bank rows, and with plain loads above.
+# up to 192 tokens with three or more bank rows (256 with two), and with
+# plain loads above.
+RANGED_ROW_MAX_T = {2: 256}   # else 192
 RANGED_ROW_CASES = [
     dict(nb=2),
     dict(nb=3, has_delta=False),
@@ -454,28 +456,30 @@ RANGED_ROW_CASES = [
 
 @pytest.mark.parametrize("kw", RANGED_ROW_CASES, ids=lambda kw: f"nb{kw['nb']}")
 def test_row_kernel_small_call_form(G, kw):
-    """The two load forms do the same arithmetic: a 129-token call (plain
-    loads) matches the oracle, and a 128-token call (range-checked loads)
-    on its first 128 tokens gives bit-identical outputs and writes."""
+    """The two load forms do the same arithmetic: a call one token past the
+    limit (plain loads) matches the oracle, and a call at the limit
+    (range-checked loads) on its first tokens gives bit-identical outputs
+    and writes."""
     from kimi_k3_attention_amd import attnres as A
-    case = W.Case(f"ranged_nb{kw['nb']}", T=129, seed=70 + kw["nb"], **kw)
+    n = RANGED_ROW_MAX_T.get(kw["nb"], 192)
+    case = W.Case(f"ranged_nb{kw['nb']}", T=n + 1, seed=70 + kw["nb"], **kw)
     inp = W.make_inputs(case)
-    G.say(case.name, "T=129")
+    G.say(case.name, f"T={n + 1}")
     d = G.upload(inp)
     G.run(d, path=A.ATTNRES_PATH_ROW)
     full = G.download(d)
     G.check_full(inp, full, G.oracle_full(inp))
-    sub = W.with_(case, T=128)
-    part_in = W.Inputs(case=sub, prefix=inp.prefix[:128].copy(),
-                       delta=None if inp.delta is None else inp.delta[:128].copy(),
+    sub = W.with_(case, T=n)
+    part_in = W.Inputs(case=sub, prefix=inp.prefix[:n].copy(),
+                       delta=None if inp.delta is None else inp.delta[:n].copy(),
                        bank=inp.bank[:sub.bank_elems].copy(), res_w=inp.res_w, rms_w=inp.rms_w,
-                       onw=inp.onw, out_init=inp.out_init[:128].copy())
-    G.say(case.name, "T=128")
+                       onw=inp.onw, out_init=inp.out_init[:n].copy())
+    G.say(case.name, f"T={n}")
     d = G.upload(part_in)
     G.run(d, path=A.ATTNRES_PATH_ROW)
     part = G.download(d)
-    assert np.array_equal(part.out, full.out[:128]), "out"
-    assert np.array_equal(part.prefix, full.prefix[:128]), "prefix"
+    assert np.array_equal(part.out, full.out[:n]), "out"
+    assert np.array_equal(part.prefix, full.prefix[:n]), "prefix"
     assert np.array_equal(part.bank, full.bank[:sub.bank_elems]), "bank"
 
 
@@ -620,15 +624,18 @@ def test_cancelling_sources(G):
 
 @pytest.mark.parametrize("path_name", ["row", "split", "any_h", "row_small"])
 def test_bank_offsets_beyond_32_bits(G, path_name):
-    """A bank whose element offsets exceed 2^31 (token stride 2^24 elements,
-    about 4.8 GB; for the row kernel's small-call form, 100 tokens 2^25
-    apart, about 6.7 GB): only the used rows are filled; sampled tokens are
-    checked against the oracle and the elements right after each written row
-    keep their sentinel."""
+    """A bank whose element offsets exceed 2^31 (150 tokens 2^24 elements
+    apart, about 4.8 GB; the row kernel takes its small-call form there, and
+    its plain form at 200 tokens, about 6.4 GB; 100 tokens 2^25 apart, about
+    6.7 GB): only the used rows are filled; sampled tokens are checked
+    against the oracle and the elements right after each written row keep
+    their sentinel."""
     from kimi_k3_attention_amd import attnres as A
     small = path_name == "row_small"
     path = A.ATTNRES_PATH_ROW if small else _path_of(path_name)
-    T, nb, cap, H, ts = (100, 5, 8, 7168, 1 << 25) if small else (150, 5, 8, 7168, 1 << 24)
+    T, nb, cap, H, ts = ((100, 5, 8, 7168, 1 << 25) if small
+                         else (200, 5, 8, 7168, 1 << 24) if path_name == "row"
+                         else (150, 5, 8, 7168, 1 << 24))
     case = W.Case("small_rows", T=T, nb=nb, cap=cap, widx=6, seed=95)
     inp = W.make_inputs(case)                      # dense bank, used for the values
     bank = torch.full((T * ts,), 0x7F81, dtype=torch.int16, device="cuda")
