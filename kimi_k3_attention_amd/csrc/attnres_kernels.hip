@@ -118,7 +118,8 @@ constexpr float kInvHidden = 1.0f / kHidden;
 // form).  Measured against plain loads, bit-identical: T = 32-176 at nb =
 // 2-8 0.3-3.7 % faster, T = 192 0.2-0.8 %; T = 208-256 0.2-1 % slower at
 // nb = 4-8 but 0.8-2.3 % faster at nb = 2; T = 384-768 slower at every nb;
-// nb = 1 no faster at any T.  nb = 3 (not measured) takes 192, as nb = 4-8.
+// nb = 1 no faster at any T.  nb = 3 at T = 208-256 and nb = 2 at 288-320:
+// within the 1.3 % spread between library copies.
 constexpr int kRowRangedMinBlocks = 2;
 constexpr int kRowRangedMaxT[kMaxBlocks + 1] = {0, 0, 256, 192, 192, 192, 192, 192, 192};
 
